@@ -1,0 +1,199 @@
+/*
+ * lcx — long-context scaled-RoPE causal GQA attention on MI355X (gfx950).
+ *
+ * C ABI of liblcx.so.  Plain pointers and sizes only.  Device pointers are
+ * HIP device memory owned by the caller; host pointers are ordinary memory.
+ * The library allocates no device memory, keeps no global state, never
+ * synchronises and never creates streams: all device work is enqueued on the
+ * caller's `stream`.  Every argument check happens before anything is
+ * enqueued; a non-OK return enqueues nothing (LCX_ERR_HIP: a launch was
+ * rejected by the runtime).  Faults inside kernels surface at the caller's
+ * next synchronisation.  No C++ exception crosses this boundary.
+ * lcx_last_error() gives a per-thread message for the last non-OK return.
+ *
+ * Sources, by page title and section:
+ *   [CE] "上下文擴充套件（Context Extension）" (compassingai.com concept page)
+ *   [CW] "上下文窗口扩展技术：从 4K 到 1M" (guijiagi.com)
+ *   [JJ] "AI 大模型窗口上下文进化史" (juejin.cn)
+ *
+ * Layouts.  Q, O: [B][Hq][n][d]; K, V: [B][Hkv][n][d]; each given by element
+ * strides {batch, head, seq}; the last dimension is contiguous.  LSE is
+ * fp32 [B][Hq][n] with strides {batch, head} and unit row stride.  RoPE
+ * tables are fp32 row-major [n_pos][d/2]: row r is position tab_pos0 + r.
+ */
+#ifndef LCX_H
+#define LCX_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LCX_OK = 0,
+  LCX_ERR_INVALID_ARG = 1, /* NULL where required, bad sizes, bad scheme parameters */
+  LCX_ERR_UNSUPPORTED = 2, /* valid request outside what the kernels implement (d not 64/128, ...) */
+  LCX_ERR_HIP = 3          /* the HIP runtime rejected a launch */
+} lcx_status;
+
+/* RoPE schemes.  s = L_target / L_train throughout.
+ *   PLAIN        theta_i = base^(-2i/d), pair (2i, 2i+1) of q/k at position m
+ *                turned by m·theta_i                        [CE 技術原理 RoPE 定義]
+ *   PI           positions scaled: m -> m·L_train/L_target   [CW §2.1; CE 位置插值]
+ *   NTK          base -> base·s^(d/(d-2))                     [CW §2.2; CE NTK-aware]
+ *   NTK_PARTS    per-pair factor by wavelength: 1 below L_train/beta, 1/s above
+ *                L_train/alpha, linear in wavelength between   [CW §2.3]
+ *   YARN         NTK_PARTS + logits divided by t = 0.1·ln(s) + 1   [CW §2.4]
+ *   DYNAMIC_NTK  base -> base·(l/L_train)^(d/(d-2)) when l > L_train, l = cur_len
+ *                                                              [CW §3 动态 NTK]  */
+typedef enum {
+  LCX_ROPE_NONE = 0,
+  LCX_ROPE_PLAIN = 1,
+  LCX_ROPE_PI = 2,
+  LCX_ROPE_NTK = 3,
+  LCX_ROPE_NTK_PARTS = 4,
+  LCX_ROPE_YARN = 5,
+  LCX_ROPE_DYNAMIC_NTK = 6
+} lcx_rope_scheme;
+
+typedef enum { LCX_BF16 = 0, LCX_F32 = 1, LCX_F16 = 2 } lcx_dtype;
+
+/* The pages' problem statement: scheme, base, head_dim, L_train, L_target and
+ * the by-parts ramp parameters ([CW §2.3] signature: head_dim, orig_len,
+ * target_len, alpha = 1, beta = 32; [CW §3] base, train_len, head_dim, l). */
+typedef struct {
+  int32_t scheme;   /* lcx_rope_scheme */
+  int32_t head_dim; /* d: even, >= 2 */
+  double base;      /* > 1 */
+  int64_t L_train;  /* > 0 for every scaling scheme */
+  int64_t L_target; /* >= L_train for every scaling scheme */
+  int64_t cur_len;  /* DYNAMIC_NTK: current length l; 0 means L_target */
+  double alpha;     /* NTK_PARTS / YARN: 0 < alpha < beta (pages: 1) */
+  double beta;      /* (pages: 32) */
+} lcx_rope_cfg;
+
+/*
+ * Step a1 + a2: scaled frequencies and the cos/sin tables.
+ *
+ * Host part (always): inv_freq[d/2] = theta'_i (fp64), *pos_factor (1/s for PI,
+ * else 1), *logit_mult (1/t for YARN, else 1).  Each output pointer may be NULL.
+ * Device part (when cos_tab and sin_tab are non-NULL): fp32 tables
+ * [n_pos][d/2], cos/sin(((pos0 + r)·pos_factor)·theta'_i); the angle is formed
+ * and evaluated in fp64 and rounded once to fp32.  Both NULL: host-only call
+ * (no HIP call is made; stream may be NULL).
+ * Errors: INVALID_ARG for cfg NULL, scheme out of range or NONE, d odd or < 2,
+ * base <= 1, L_train <= 0 or L_target < L_train (scaling schemes), alpha/beta
+ * outside 0 < alpha < beta (NTK_PARTS/YARN), exactly one table pointer NULL,
+ * n_pos < 0, pos0 < 0.
+ */
+lcx_status lcx_rope_freqs(const lcx_rope_cfg* cfg, int64_t pos0, int64_t n_pos, double* inv_freq,
+                          double* pos_factor, double* logit_mult, float* cos_tab, float* sin_tab,
+                          hipStream_t stream);
+
+/*
+ * Step a3, standalone: rotate q [B][Hq][n][d] and/or k [B][Hkv][n][d] (bf16) at
+ * positions pos0 .. pos0+n-1 with the tables from lcx_rope_freqs; V is never
+ * rotated.  [CE 技術原理: q_m = R(m)·W_q·x_m, k_n = R(n)·W_k·x_n]
+ * out_dtype: LCX_BF16 or LCX_F16 (the f16 form keeps 3 more mantissa bits for
+ * the QK^T product).  Either (q, q_out) or (k, k_out) may be NULL/NULL.
+ * In place (q_out == q) only for LCX_BF16 with identical strides.
+ * Errors: INVALID_ARG for bad sizes, a NULL input with a non-NULL output (or
+ * the reverse), table range not covering [pos0, pos0+n); UNSUPPORTED for d
+ * not a multiple of 8 or misaligned rows (16-byte).
+ */
+lcx_status lcx_rope_apply_qk(const void* q, void* q_out, const void* k, void* k_out,
+                             int32_t out_dtype, int32_t B, int32_t Hq, int32_t Hkv, int64_t n,
+                             int32_t d, const int64_t q_strides[3], const int64_t qo_strides[3],
+                             const int64_t k_strides[3], const int64_t ko_strides[3], int64_t pos0,
+                             const float* cos_tab, const float* sin_tab, int64_t tab_pos0,
+                             int64_t tab_len, hipStream_t stream);
+
+/* Arguments of lcx_attn_fwd. */
+typedef struct {
+  const void* q; /* [B][Hq][n_q][d]; bf16 raw (rope_q = 1) or pre-rotated bf16/f16 */
+  const void* k; /* [B][Hkv][n_kv][d]; bf16 raw (rope_k = 1) or pre-rotated bf16/f16 */
+  const void* v; /* [B][Hkv][n_kv][d]; bf16, never rotated */
+  int32_t q_dtype, k_dtype; /* LCX_BF16 or LCX_F16 (F16 only when pre-rotated) */
+  int32_t B, Hq, Hkv, d;    /* Hq % Hkv == 0; d in {64, 128} */
+  int64_t n_q, n_kv;
+  int64_t q_strides[3], k_strides[3], v_strides[3], o_strides[3]; /* elements */
+  int64_t lse_strides[2];                                         /* elements: batch, head */
+  int64_t q_pos0, k_pos0; /* absolute position of row 0 / key 0 (chunks, ring share) */
+  int32_t rope_q, rope_k; /* 1: rotate while loading the tile, from the tables */
+  const float* cos_tab;   /* tables from lcx_rope_freqs; required if rope_q or rope_k */
+  const float* sin_tab;
+  int64_t tab_pos0, tab_len;
+  const lcx_rope_cfg* rope; /* optional: supplies the YaRN logit multiplier */
+  float softmax_scale;      /* 0: (1/sqrt(d))·logit_mult(rope) */
+  int32_t causal;           /* must be 1 */
+  int64_t window;           /* -1: none; else key kept iff pos_k >= pos_q - window ... */
+  int32_t n_sink;           /* ... or pos_k < n_sink  [CW §4.1, §4.2] */
+  void* o;                  /* [B][Hq][n_q][d], o_dtype */
+  int32_t o_dtype;          /* LCX_BF16 or LCX_F32 */
+  float* lse;               /* fp32 [B][Hq][n_q], natural log; -inf for a row with no key */
+  int32_t accumulate;       /* 1: merge into the existing (o f32, lse) in the epilogue */
+} lcx_attn_args;
+
+/*
+ * Steps a3 (fused) - a8: blockwise causal GQA attention with online softmax.
+ *   S = sigma·Q~K~^T over kept keys, P = softmax(S), O = P·V, LSE = ln sum exp S
+ * [JJ §4 scaled dot-product attention; CE FlashAttention 的分塊計算策略 (tiles,
+ * running max, accumulated output); CE 第二層 (GQA: query head h reads KV head
+ * floor(h·Hkv/Hq)); CW §4.1 SWA; CW §4.2 attention sinks].
+ * QK^T runs on f16 MFMA (rotated q/k rounded once to f16), PV on bf16 MFMA
+ * (P rounded to bf16), fp32 accumulation and softmax.
+ * Errors: INVALID_ARG for NULL q/k/v/o/lse, sizes <= 0 (n_kv may be 0: all
+ * rows empty), Hq % Hkv != 0, window < -1, n_sink < 0, tables missing or not
+ * covering the rotated positions, accumulate with a bf16 o, f16 with rope on;
+ * UNSUPPORTED for d not 64/128, causal == 0, non-16-byte-aligned rows.
+ */
+lcx_status lcx_attn_fwd(const lcx_attn_args* a, hipStream_t stream);
+
+/*
+ * Step a9: acc <- merge(acc, part) row by row over [B][H][rows]:
+ *   L = max(La, Lb) + log1p(exp(-|La - Lb|)),  O = e^(La-L)·Oa + e^(Lb-L)·Ob,
+ * a -inf partial being the identity.  [CE FlashAttention running-max merge;
+ * CW §5.3 per-step partial attention merged into the output]
+ * O tensors fp32 with element strides {batch, head, row}; LSE strides
+ * {batch, head}, unit row stride.  o_final (optional, LCX_BF16 or LCX_F32) also
+ * receives the merged O.
+ * Errors: INVALID_ARG for NULL required pointers or bad sizes; UNSUPPORTED for
+ * d not a multiple of 4.
+ */
+lcx_status lcx_attn_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
+                          int32_t B, int32_t H, int64_t rows, int32_t d,
+                          const int64_t acc_strides[3], const int64_t part_strides[3],
+                          const int64_t lse_acc_strides[2], const int64_t lse_part_strides[2],
+                          void* o_final, int32_t o_final_dtype, const int64_t final_strides[3],
+                          hipStream_t stream);
+
+/*
+ * Step a10: the single-GPU share of ring attention.  Keys are taken in chunks
+ * of `chunk` (KV block c at key positions k_pos0 + c·chunk ..), each chunk's
+ * partial attention is computed for the query rows that can see it and merged
+ * into (o_acc, lse_acc) — fp32 [B][Hq][n_q][d] and [B][Hq][n_q], contiguous,
+ * caller-owned.  With o_part/lse_part (same shapes) non-NULL each chunk is
+ * written there and merged by lcx_attn_merge; with both NULL the merge runs in
+ * the attention epilogue.  At the end a->o receives the result in a->o_dtype
+ * and a->lse the LSE (a->o may be o_acc itself when o_dtype is F32, likewise
+ * a->lse may be lse_acc).  [CW §5.1-5.4 Ring Attention; kwkr.cn news 38338
+ * §2.2 ring computation with online aggregation]
+ * Errors: as lcx_attn_fwd, plus INVALID_ARG for chunk <= 0, NULL o_acc/lse_acc,
+ * exactly one of o_part/lse_part NULL, a->accumulate != 0.
+ */
+lcx_status lcx_attn_fwd_chunked(const lcx_attn_args* a, int64_t chunk, float* o_acc, float* lse_acc,
+                                float* o_part, float* lse_part, hipStream_t stream);
+
+/* Name of a status code (static string). */
+const char* lcx_status_string(lcx_status s);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* lcx_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCX_H */

@@ -1,0 +1,221 @@
+"""Python binding of liblcx (scaled-RoPE causal GQA attention for MI355X).
+
+Argument marshalling only: torch tensors supply device memory, strides and the
+current HIP stream; every step of the computation runs in the library's gfx950
+kernels behind the C ABI of ``include/lcx.h``.  If ``liblcx.so`` has not been
+built, importing this package fails; there is no other implementation to fall
+back on.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblcx.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; "
+                      f"g.build()' or python long_context_attention_rope_amd/_build.py)")
+_lib = ctypes.CDLL(LIB_PATH)
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
+SCHEMES = {"none": 0, "plain": 1, "pi": 2, "ntk": 3, "ntk_parts": 4, "yarn": 5, "dynamic_ntk": 6}
+BF16, F32, F16 = 0, 1, 2
+_DT = {torch.bfloat16: BF16, torch.float32: F32, torch.float16: F16}
+
+_i32, _i64, _f64, _f32, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_double, ctypes.c_float, ctypes.c_void_p
+
+
+class RopeCfg(ctypes.Structure):
+    _fields_ = [("scheme", _i32), ("head_dim", _i32), ("base", _f64), ("L_train", _i64),
+                ("L_target", _i64), ("cur_len", _i64), ("alpha", _f64), ("beta", _f64)]
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [("q", _vp), ("k", _vp), ("v", _vp), ("q_dtype", _i32), ("k_dtype", _i32),
+                ("B", _i32), ("Hq", _i32), ("Hkv", _i32), ("d", _i32),
+                ("n_q", _i64), ("n_kv", _i64),
+                ("q_strides", _i64 * 3), ("k_strides", _i64 * 3), ("v_strides", _i64 * 3),
+                ("o_strides", _i64 * 3), ("lse_strides", _i64 * 2),
+                ("q_pos0", _i64), ("k_pos0", _i64), ("rope_q", _i32), ("rope_k", _i32),
+                ("cos_tab", _vp), ("sin_tab", _vp), ("tab_pos0", _i64), ("tab_len", _i64),
+                ("rope", ctypes.POINTER(RopeCfg)), ("softmax_scale", _f32), ("causal", _i32),
+                ("window", _i64), ("n_sink", _i32), ("o", _vp), ("o_dtype", _i32),
+                ("lse", _vp), ("accumulate", _i32)]
+
+
+_P3 = ctypes.POINTER(_i64)
+_lib.lcx_status_string.argtypes = [ctypes.c_int]
+_lib.lcx_status_string.restype = ctypes.c_char_p
+_lib.lcx_last_error.argtypes = []
+_lib.lcx_last_error.restype = ctypes.c_char_p
+_lib.lcx_rope_freqs.argtypes = [ctypes.POINTER(RopeCfg), _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.lcx_rope_freqs.restype = ctypes.c_int
+_lib.lcx_rope_apply_qk.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32,
+                                   _P3, _P3, _P3, _P3, _i64, _vp, _vp, _i64, _i64, _vp]
+_lib.lcx_rope_apply_qk.restype = ctypes.c_int
+_lib.lcx_attn_fwd.argtypes = [ctypes.POINTER(AttnArgs), _vp]
+_lib.lcx_attn_fwd.restype = ctypes.c_int
+_lib.lcx_attn_merge.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i64, _i32, _P3, _P3, _P3, _P3,
+                                _vp, _i32, _P3, _vp]
+_lib.lcx_attn_merge.restype = ctypes.c_int
+_lib.lcx_attn_fwd_chunked.argtypes = [ctypes.POINTER(AttnArgs), _i64, _vp, _vp, _vp, _vp, _vp]
+_lib.lcx_attn_fwd_chunked.restype = ctypes.c_int
+
+
+class LcxError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        name = _lib.lcx_status_string(status).decode()
+        super().__init__(f"{name}: {message}")
+
+
+def _check(st: int):
+    if st != OK:
+        raise LcxError(st, _lib.lcx_last_error().decode())
+
+
+def _stream(t: torch.Tensor | None):
+    if t is None or not t.is_cuda:
+        return None
+    return _vp(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else _vp(t.data_ptr())
+
+
+def _s3(t):
+    return (_i64 * 3)(*t.stride()[:3]) if t is not None else None
+
+
+def _s2(t):
+    return (_i64 * 2)(*t.stride()[:2])
+
+
+def rope_cfg(scheme: str, base: float, head_dim: int, L_train: int = 1, L_target: int = 1,
+             cur_len: int = 0, alpha: float = 1.0, beta: float = 32.0) -> RopeCfg:
+    return RopeCfg(SCHEMES[scheme], head_dim, base, L_train, L_target, cur_len, alpha, beta)
+
+
+def rope_freqs(cfg: RopeCfg, cos: torch.Tensor | None = None, sin: torch.Tensor | None = None,
+               pos0: int = 0):
+    """lcx_rope_freqs: returns (inv_freq list, pos_factor, logit_mult); fills cos/sin
+    (fp32 [n_pos][d/2] device tensors) when given."""
+    half = cfg.head_dim // 2
+    inv = (_f64 * max(half, 1))()
+    pf, lm = _f64(0), _f64(0)
+    n_pos = cos.shape[0] if cos is not None else 0
+    _check(_lib.lcx_rope_freqs(ctypes.byref(cfg), pos0, n_pos, ctypes.cast(inv, _vp),
+                               _vp(ctypes.addressof(pf)), _vp(ctypes.addressof(lm)), _ptr(cos),
+                               _ptr(sin), _stream(cos)))
+    return list(inv)[:half], pf.value, lm.value
+
+
+def rope_tables(cfg: RopeCfg, n_pos: int, pos0: int = 0, device="cuda"):
+    """Allocate and fill the fp32 cos/sin tables [n_pos][d/2] for positions pos0.."""
+    half = cfg.head_dim // 2
+    cos = torch.empty((n_pos, half), dtype=torch.float32, device=device)
+    sin = torch.empty((n_pos, half), dtype=torch.float32, device=device)
+    rope_freqs(cfg, cos, sin, pos0)
+    return cos, sin
+
+
+def rope_apply_qk(q, k, cos, sin, *, pos0: int = 0, tab_pos0: int = 0, q_out=None, k_out=None,
+                  out_dtype=torch.float16):
+    """lcx_rope_apply_qk on [B, H, n, d] bf16 tensors (either may be None).
+    Outputs are allocated with torch when not given; returns (q_out, k_out)."""
+    if q is not None and q_out is None:
+        q_out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    if k is not None and k_out is None:
+        k_out = torch.empty(k.shape, dtype=out_dtype, device=k.device)
+    ref = q if q is not None else k
+    B, _, n, d = ref.shape
+    Hq = q.shape[1] if q is not None else 0
+    Hkv = k.shape[1] if k is not None else 0
+    od = _DT[(q_out if q_out is not None else k_out).dtype]
+    _check(_lib.lcx_rope_apply_qk(_ptr(q), _ptr(q_out), _ptr(k), _ptr(k_out), od, B, Hq, Hkv, n, d,
+                                  _s3(q), _s3(q_out), _s3(k), _s3(k_out), pos0, _ptr(cos), _ptr(sin),
+                                  tab_pos0, cos.shape[0], _stream(ref)))
+    return q_out, k_out
+
+
+def _attn_args(q, k, v, o, lse, *, rope_q, rope_k, cos, sin, tab_pos0, cfg, softmax_scale,
+               window, n_sink, q_pos0, k_pos0, accumulate, causal=True):
+    B, Hq, n_q, d = q.shape
+    Hkv, n_kv = k.shape[1], k.shape[2]
+    a = AttnArgs()
+    a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    a.q_dtype, a.k_dtype = _DT[q.dtype], _DT[k.dtype]
+    a.B, a.Hq, a.Hkv, a.d = B, Hq, Hkv, d
+    a.n_q, a.n_kv = n_q, n_kv
+    a.q_strides, a.k_strides, a.v_strides = _s3(q), _s3(k), _s3(v)
+    a.o_strides = _s3(o)
+    if lse.stride(2) != 1:
+        raise ValueError("lse rows must be contiguous")
+    a.lse_strides = _s2(lse)
+    a.q_pos0, a.k_pos0 = q_pos0, k_pos0
+    a.rope_q, a.rope_k = int(rope_q), int(rope_k)
+    a.cos_tab = cos.data_ptr() if cos is not None else None
+    a.sin_tab = sin.data_ptr() if sin is not None else None
+    a.tab_pos0 = tab_pos0
+    a.tab_len = cos.shape[0] if cos is not None else 0
+    a.rope = ctypes.pointer(cfg) if cfg is not None else None
+    a.softmax_scale = softmax_scale
+    a.causal = int(causal)
+    a.window, a.n_sink = window, n_sink
+    a.o, a.o_dtype = o.data_ptr(), _DT[o.dtype]
+    a.lse = lse.data_ptr()
+    a.accumulate = int(accumulate)
+    return a
+
+
+def attn_fwd(q, k, v, o=None, lse=None, *, rope_q=False, rope_k=False, cos=None, sin=None,
+             tab_pos0=0, rope=None, softmax_scale=0.0, window=-1, n_sink=0, q_pos0=0, k_pos0=0,
+             accumulate=False, out_dtype=torch.bfloat16, causal=True):
+    """lcx_attn_fwd.  q [B,Hq,n_q,d], k/v [B,Hkv,n_kv,d].  Returns (o, lse)."""
+    B, Hq, n_q, d = q.shape
+    if o is None:
+        o = torch.empty((B, Hq, n_q, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, n_q), dtype=torch.float32, device=q.device)
+    a = _attn_args(q, k, v, o, lse, rope_q=rope_q, rope_k=rope_k, cos=cos, sin=sin,
+                   tab_pos0=tab_pos0, cfg=rope, softmax_scale=softmax_scale, window=window,
+                   n_sink=n_sink, q_pos0=q_pos0, k_pos0=k_pos0, accumulate=accumulate,
+                   causal=causal)
+    _check(_lib.lcx_attn_fwd(ctypes.byref(a), _stream(q)))
+    return o, lse
+
+
+def attn_fwd_chunked(q, k, v, chunk: int, o_acc, lse_acc, o=None, lse=None, *, o_part=None,
+                     lse_part=None, rope_q=False, rope_k=False, cos=None, sin=None, tab_pos0=0,
+                     rope=None, softmax_scale=0.0, window=-1, n_sink=0, q_pos0=0, k_pos0=0,
+                     out_dtype=torch.bfloat16):
+    """lcx_attn_fwd_chunked.  o_acc fp32 [B,Hq,n_q,d] / lse_acc fp32 [B,Hq,n_q] workspace;
+    o_part/lse_part (same shapes) select the separate merge pass.  Returns (o, lse)."""
+    B, Hq, n_q, d = q.shape
+    if o is None:
+        o = torch.empty((B, Hq, n_q, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, n_q), dtype=torch.float32, device=q.device)
+    a = _attn_args(q, k, v, o, lse, rope_q=rope_q, rope_k=rope_k, cos=cos, sin=sin,
+                   tab_pos0=tab_pos0, cfg=rope, softmax_scale=softmax_scale, window=window,
+                   n_sink=n_sink, q_pos0=q_pos0, k_pos0=k_pos0, accumulate=False)
+    _check(_lib.lcx_attn_fwd_chunked(ctypes.byref(a), chunk, _ptr(o_acc), _ptr(lse_acc),
+                                     _ptr(o_part), _ptr(lse_part), _stream(q)))
+    return o, lse
+
+
+def attn_merge(o_acc, lse_acc, o_part, lse_part, o_final=None):
+    """lcx_attn_merge over [B,H,rows,d] fp32 tensors (in place into o_acc/lse_acc)."""
+    B, H, rows, d = o_acc.shape
+    if lse_acc.stride(2) != 1 or lse_part.stride(2) != 1:
+        raise ValueError("lse rows must be contiguous")
+    fdt = _DT[o_final.dtype] if o_final is not None else BF16
+    _check(_lib.lcx_attn_merge(_ptr(o_acc), _ptr(lse_acc), _ptr(o_part), _ptr(lse_part), B, H, rows, d,
+                               _s3(o_acc), _s3(o_part), _s2(lse_acc), _s2(lse_part), _ptr(o_final),
+                               fdt, _s3(o_final) if o_final is not None else None, _stream(o_acc)))
+    return o_acc, lse_acc

@@ -1,0 +1,163 @@
+// Merge of partial attention results (step a9) and helpers of the chunked
+// driver (step a10).
+//
+// Two results (O_a, L_a), (O_b, L_b) of the same query row over disjoint key
+// sets combine exactly as
+//   L = max(L_a, L_b) + log1p(exp(-|L_a - L_b|)),  O = e^(L_a-L) O_a + e^(L_b-L) O_b
+// — the running-max rescaling of "上下文擴充套件（Context Extension）",
+// FlashAttention 的分塊計算策略, written with log-sum-exp; it is what each ring
+// step of "上下文窗口扩展技术：从 4K 到 1M" §5.3 needs (the listing's plain "+="
+// of partial outputs would weight the blocks wrongly).  L = -inf is an empty
+// partial and acts as the identity.
+//
+// HBM-bound: one workgroup of up to 256 threads covers whole rows (d/4
+// threads per row, 16 bytes each); every thread of a row reads both LSEs
+// before the barrier, one thread writes the merged LSE after it.
+#include "lcx_device.h"
+#include "lcx_internal.h"
+
+namespace lcx {
+
+__global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams p, int rows_per_block) {
+  const int tpr = p.d >> 2;  // threads per row
+  const int lr = threadIdx.x / tpr;
+  const int c = threadIdx.x - lr * tpr;
+  const int64_t flat = (int64_t)blockIdx.x * rows_per_block + lr;  // over B*H*rows
+  const int64_t total = (int64_t)p.B * p.H * p.rows;
+  const bool active = lr < rows_per_block && flat < total;
+  float la = -INFINITY, lb = -INFINITY;
+  int64_t r = 0, bh = 0;
+  int b = 0, h = 0;
+  if (active) {
+    r = flat % p.rows;
+    bh = flat / p.rows;
+    h = (int)(bh % p.H);
+    b = (int)(bh / p.H);
+    la = p.lse_acc[b * p.la_b + h * p.la_h + r];
+    lb = p.lse_part[b * p.lp_b + h * p.lp_h + r];
+  }
+  __syncthreads();  // every old LSE is read before any is overwritten
+  if (!active) return;
+  float wa, wb, L;
+  if (lb == -INFINITY) {
+    wa = 1.f; wb = 0.f; L = la;
+  } else if (la == -INFINITY) {
+    wa = 0.f; wb = 1.f; L = lb;
+  } else {
+    const float mx = fmaxf(la, lb), mn = fminf(la, lb);
+    L = mx + log1pf(expf(mn - mx));
+    wa = expf(la - L);
+    wb = expf(lb - L);
+  }
+  float* oa = p.o_acc + b * p.as_b + h * p.as_h + r * p.as_s + 4 * c;
+  const float* ob = p.o_part + b * p.ps_b + h * p.ps_h + r * p.ps_s + 4 * c;
+  const f32x4 va = *reinterpret_cast<const f32x4*>(oa);
+  const f32x4 vb = *reinterpret_cast<const f32x4*>(ob);
+  f32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = (wa == 0.f ? 0.f : wa * va[e]) + (wb == 0.f ? 0.f : wb * vb[e]);
+  *reinterpret_cast<f32x4*>(oa) = o;
+  if (p.o_final) {
+    if (p.final_f32) {
+      float* of = static_cast<float*>(p.o_final) + b * p.fs_b + h * p.fs_h + r * p.fs_s + 4 * c;
+      *reinterpret_cast<f32x4*>(of) = o;
+    } else {
+      uint16_t* of = static_cast<uint16_t*>(p.o_final) + b * p.fs_b + h * p.fs_h + r * p.fs_s + 4 * c;
+      u32x2 w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+      *reinterpret_cast<u32x2*>(of) = w;
+    }
+  }
+  if (c == 0) p.lse_acc[b * p.la_b + h * p.la_h + r] = L;
+}
+
+hipError_t launch_attn_merge(const MergeParams& p, hipStream_t s) {
+  const int tpr = p.d / 4;
+  const int rpb = tpr >= 256 ? 1 : 256 / tpr;
+  const int64_t total = (int64_t)p.B * p.H * p.rows;
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = (total + rpb - 1) / rpb;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)blocks), dim3(rpb * tpr), 0, s, p, rpb);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void fill_empty_kernel(float* o, float* lse, int32_t B, int32_t H,
+                                                         int64_t rows, int32_t d, int64_t os_b,
+                                                         int64_t os_h, int64_t os_s, int64_t ls_b,
+                                                         int64_t ls_h) {
+  const int tpr = d >> 2;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t flat = t / tpr;
+  const int c = (int)(t - flat * tpr);
+  if (flat >= (int64_t)B * H * rows) return;
+  const int64_t r = flat % rows;
+  const int64_t bh = flat / rows;
+  const int h = (int)(bh % H), b = (int)(bh / H);
+  f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  *reinterpret_cast<f32x4*>(o + b * os_b + h * os_h + r * os_s + 4 * c) = z;
+  if (c == 0) lse[b * ls_b + h * ls_h + r] = -INFINITY;
+}
+
+hipError_t launch_fill_empty(float* o, float* lse, int32_t B, int32_t H, int64_t rows, int32_t d,
+                             int64_t os_b, int64_t os_h, int64_t os_s, int64_t ls_b, int64_t ls_h,
+                             hipStream_t s) {
+  const int64_t total = (int64_t)B * H * rows * (d / 4);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_empty_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, o,
+                     lse, B, H, rows, d, os_b, os_h, os_s, ls_b, ls_h);
+  return hipGetLastError();
+}
+
+struct FinalizeParams {
+  const float* o_acc;
+  const float* lse_acc;
+  void* o;
+  float* lse;
+  int32_t o_f32, copy_o, copy_lse;
+  int32_t B, H, d;
+  int64_t rows;
+  int64_t as_b, as_h, as_s, la_b, la_h;
+  int64_t os_b, os_h, os_s, ls_b, ls_h;
+};
+
+__global__ __launch_bounds__(256) void finalize_kernel(FinalizeParams p) {
+  const int tpr = p.d >> 2;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t flat = t / tpr;
+  const int c = (int)(t - flat * tpr);
+  if (flat >= (int64_t)p.B * p.H * p.rows) return;
+  const int64_t r = flat % p.rows;
+  const int64_t bh = flat / p.rows;
+  const int h = (int)(bh % p.H), b = (int)(bh / p.H);
+  if (p.copy_o) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(p.o_acc + b * p.as_b + h * p.as_h + r * p.as_s + 4 * c);
+    if (p.o_f32) {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(p.o) + b * p.os_b + h * p.os_h + r * p.os_s + 4 * c) = v;
+    } else {
+      u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o) + b * p.os_b + h * p.os_h + r * p.os_s + 4 * c) = w;
+    }
+  }
+  if (p.copy_lse && c == 0) p.lse[b * p.ls_b + h * p.ls_h + r] = p.lse_acc[b * p.la_b + h * p.la_h + r];
+}
+
+hipError_t launch_finalize(const float* o_acc, const float* lse_acc, void* o, int32_t o_f32,
+                           float* lse, int32_t B, int32_t H, int64_t rows, int32_t d,
+                           const int64_t acc_st[3], const int64_t lse_acc_st[2],
+                           const int64_t o_st[3], const int64_t lse_st[2], hipStream_t s) {
+  FinalizeParams p{};
+  p.o_acc = o_acc; p.lse_acc = lse_acc; p.o = o; p.lse = lse;
+  p.o_f32 = o_f32;
+  p.copy_o = (o != (const void*)o_acc) ? 1 : 0;
+  p.copy_lse = (lse != lse_acc) ? 1 : 0;
+  p.B = B; p.H = H; p.d = d; p.rows = rows;
+  p.as_b = acc_st[0]; p.as_h = acc_st[1]; p.as_s = acc_st[2];
+  p.la_b = lse_acc_st[0]; p.la_h = lse_acc_st[1];
+  p.os_b = o_st[0]; p.os_h = o_st[1]; p.os_s = o_st[2];
+  p.ls_b = lse_st[0]; p.ls_h = lse_st[1];
+  const int64_t total = (int64_t)B * H * rows * (d / 4);
+  if (total == 0 || (!p.copy_o && !p.copy_lse)) return hipSuccess;
+  hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace lcx

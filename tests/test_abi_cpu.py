@@ -1,0 +1,176 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, computes the scheme frequencies on the host like the oracle,
+and rejects bad arguments before touching the device."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lcx.h")
+
+
+@pytest.fixture(scope="module")
+def lcx():
+    import long_context_attention_rope_amd as m
+    return m
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:lcx_status|const char\*)\s+(lcx_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared() == sorted(["lcx_rope_freqs", "lcx_rope_apply_qk", "lcx_attn_fwd",
+                                  "lcx_attn_merge", "lcx_attn_fwd_chunked", "lcx_status_string",
+                                  "lcx_last_error"])
+
+
+def test_library_exports_every_declared_symbol(lcx):
+    out = subprocess.run(["nm", "-D", "--defined-only", lcx.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (lcx_\w+)", out))
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(lcx._lib, name)
+
+
+def test_library_has_gfx950_code_object(lcx):
+    data = open(lcx.LIB_PATH, "rb").read()
+    assert b"gfx950" in data
+
+
+def test_status_strings(lcx):
+    assert lcx._lib.lcx_status_string(0) == b"LCX_OK"
+    assert lcx._lib.lcx_status_string(2) == b"LCX_ERR_UNSUPPORTED"
+
+
+CFGS = [
+    ("plain", 10000.0, 64, 128, 512, 0),
+    ("pi", 500000.0, 128, 8192, 65536, 0),
+    ("ntk", 10000.0, 64, 128, 512, 0),
+    ("ntk", 500000.0, 128, 8192, 1048576, 0),
+    ("ntk_parts", 500000.0, 128, 8192, 32768, 0),
+    ("yarn", 500000.0, 128, 8192, 32768, 0),
+    ("dynamic_ntk", 500000.0, 128, 8192, 131072, 131072),
+    ("dynamic_ntk", 500000.0, 128, 8192, 131072, 4096),
+]
+
+
+@pytest.mark.parametrize("scheme,base,d,Lt,Lg,cur", CFGS)
+def test_host_scheme_math_matches_oracle(lcx, scheme, base, d, Lt, Lg, cur):
+    cfg = lcx.rope_cfg(scheme, base, d, Lt, Lg, cur, 1.0, 32.0)
+    th, pf, lm = lcx.rope_freqs(cfg)
+    th_o, pf_o, lm_o = oracle.rope_freqs(scheme, base, d, Lt, Lg, cur, 1.0, 32.0)
+    np.testing.assert_allclose(np.array(th), th_o, rtol=1e-15, atol=0)
+    assert pf == pytest.approx(pf_o, rel=1e-15) and lm == pytest.approx(lm_o, rel=1e-15)
+
+
+def test_yarn_8b_softmax_constants(lcx):
+    # the Llama-3-8B-shaped workload: s = 4, t = 0.1 ln 4 + 1
+    _, _, lm = lcx.rope_freqs(lcx.rope_cfg("yarn", 500000.0, 128, 8192, 32768))
+    assert 1 / lm == pytest.approx(1.1386294361119891, rel=1e-14)
+
+
+def _st(lcx, status, fn):
+    with pytest.raises(lcx.LcxError) as e:
+        fn()
+    assert e.value.status == status, str(e.value)
+    assert len(lcx._lib.lcx_last_error()) > 0
+
+
+@pytest.mark.parametrize("bad", [
+    dict(scheme="plain", base=10000.0, head_dim=63),
+    dict(scheme="plain", base=1.0, head_dim=64),
+    dict(scheme="ntk", base=10000.0, head_dim=64, L_train=8192, L_target=4096),
+    dict(scheme="pi", base=10000.0, head_dim=64, L_train=0, L_target=4096),
+    dict(scheme="yarn", base=10000.0, head_dim=64, L_train=8, L_target=32, alpha=32.0, beta=1.0),
+    dict(scheme="none", base=10000.0, head_dim=64),
+])
+def test_rope_freqs_rejects(lcx, bad):
+    cfg = lcx.rope_cfg(**bad)
+    _st(lcx, lcx.ERR_INVALID_ARG, lambda: lcx.rope_freqs(cfg))
+
+
+def test_rope_freqs_one_table_pointer(lcx):
+    cfg = lcx.rope_cfg("plain", 10000.0, 64)
+    st = lcx._lib.lcx_rope_freqs(ctypes.byref(cfg), 0, 16, None, None, None, ctypes.c_void_p(4096),
+                                 None, None)
+    assert st == lcx.ERR_INVALID_ARG
+
+
+FAKE = 1 << 20  # never dereferenced: every case below fails validation first
+
+
+def _args(lcx, **kw):
+    a = lcx.AttnArgs()
+    a.q = a.k = a.v = a.o = a.lse = FAKE
+    a.q_dtype = a.k_dtype = lcx.BF16
+    a.B, a.Hq, a.Hkv, a.d = 1, 4, 1, 64
+    a.n_q = a.n_kv = 256
+    a.q_strides = (ctypes.c_int64 * 3)(4 * 256 * 64, 256 * 64, 64)
+    a.k_strides = (ctypes.c_int64 * 3)(256 * 64, 256 * 64, 64)
+    a.v_strides = (ctypes.c_int64 * 3)(256 * 64, 256 * 64, 64)
+    a.o_strides = (ctypes.c_int64 * 3)(4 * 256 * 64, 256 * 64, 64)
+    a.lse_strides = (ctypes.c_int64 * 2)(4 * 256, 256)
+    a.causal = 1
+    a.window = -1
+    a.o_dtype = lcx.BF16
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+ATTN_BAD = [
+    (1, dict(q=None)), (1, dict(lse=None)), (1, dict(Hq=6, Hkv=4)), (1, dict(B=0)),
+    (1, dict(n_q=-1)), (2, dict(d=96)), (2, dict(d=256)), (2, dict(causal=0)), (1, dict(window=-2)),
+    (1, dict(n_sink=-1)), (1, dict(rope_q=1)), (1, dict(rope_q=1, q_dtype=2, cos_tab=FAKE, sin_tab=FAKE, tab_len=256)),
+    (1, dict(rope_k=1, cos_tab=FAKE, sin_tab=FAKE, tab_len=100)),
+    (1, dict(rope_q=1, cos_tab=FAKE, sin_tab=FAKE, tab_len=256, q_pos0=1)),
+    (1, dict(accumulate=1)), (1, dict(o_dtype=7)), (1, dict(softmax_scale=-1.0)),
+    (2, dict(q=FAKE + 2)), (2, dict(q_strides=(ctypes.c_int64 * 3)(0, 0, 60))),
+]
+
+
+@pytest.mark.parametrize("status,kw", ATTN_BAD)
+def test_attn_fwd_rejects_before_launch(lcx, status, kw):
+    a = _args(lcx, **kw)
+    assert lcx._lib.lcx_attn_fwd(ctypes.byref(a), None) == status, lcx._lib.lcx_last_error()
+
+
+def test_chunked_rejects(lcx):
+    a = _args(lcx, o_dtype=lcx.F32)
+    assert lcx._lib.lcx_attn_fwd_chunked(ctypes.byref(a), 0, FAKE, FAKE, None, None, None) == 1
+    assert lcx._lib.lcx_attn_fwd_chunked(ctypes.byref(a), 64, None, FAKE, None, None, None) == 1
+    assert lcx._lib.lcx_attn_fwd_chunked(ctypes.byref(a), 64, FAKE, FAKE, FAKE, None, None) == 1
+    a2 = _args(lcx, o_dtype=lcx.F32, accumulate=1)
+    assert lcx._lib.lcx_attn_fwd_chunked(ctypes.byref(a2), 64, FAKE, FAKE, None, None, None) == 1
+
+
+def test_rope_apply_rejects(lcx):
+    P3 = ctypes.c_int64 * 3
+    st = P3(256 * 64, 256 * 64, 64)
+    f = lcx._lib.lcx_rope_apply_qk
+    # output without input
+    assert f(None, FAKE, None, None, lcx.F16, 1, 1, 1, 256, 64, st, st, st, st, 0, FAKE, FAKE, 0, 256, None) == 1
+    # table too short
+    assert f(FAKE, FAKE, None, None, lcx.F16, 1, 1, 1, 256, 64, st, st, st, st, 0, FAKE, FAKE, 0, 255, None) == 1
+    # in place in f16
+    assert f(FAKE, FAKE, None, None, lcx.F16, 1, 1, 1, 256, 64, st, st, st, st, 0, FAKE, FAKE, 0, 256, None) == 1
+    # d not a multiple of 8
+    assert f(FAKE, FAKE + 4096, None, None, lcx.F16, 1, 1, 1, 256, 60, st, st, st, st, 0, FAKE, FAKE, 0, 256, None) == 2
+
+
+def test_merge_rejects(lcx):
+    P3, P2 = ctypes.c_int64 * 3, ctypes.c_int64 * 2
+    s3, s2 = P3(4096, 4096, 64), P2(64, 64)
+    f = lcx._lib.lcx_attn_merge
+    assert f(None, FAKE, FAKE, FAKE, 1, 1, 64, 64, s3, s3, s2, s2, None, 0, None, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 62, s3, s3, s2, s2, None, 0, None, None) == 2

@@ -1,0 +1,285 @@
+"""GPU parity of the HIP path against the fp64 oracle at sizes the oracle
+finishes in seconds: every row compared, several tiles plus ragged tails,
+all RoPE schemes, GQA ratios, masks, the chunked merge and edge cases.
+Everything goes through the C ABI (Python binding -> liblcx.so)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fixtures import workloads as W
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lcx():
+    import long_context_attention_rope_amd as m
+    return m
+
+
+def _cfg(lcx, w):
+    return lcx.rope_cfg(w.scheme, w.base, w.d, w.L_train, w.L_target, w.cur_len, w.alpha, w.beta)
+
+
+def _run(lcx, w, q, k, v, *, k_mode="pre_f16", out_dtype=torch.bfloat16, q_pos0=0, k_pos0=0,
+         tab_n=None):
+    qd, kd, vd = U.to_dev(q), U.to_dev(k), U.to_dev(v)
+    cfg = _cfg(lcx, w)
+    n_tab = tab_n or max(q_pos0 + q.shape[2], k_pos0 + k.shape[2])
+    cos, sin = lcx.rope_tables(cfg, n_tab, device=U.dev())
+    if k_mode == "fused":
+        o, lse = lcx.attn_fwd(qd, kd, vd, rope_q=True, rope_k=True, cos=cos, sin=sin, rope=cfg,
+                              window=w.window, n_sink=w.n_sink, q_pos0=q_pos0, k_pos0=k_pos0,
+                              out_dtype=out_dtype)
+    else:
+        odt = torch.float16 if k_mode == "pre_f16" else torch.bfloat16
+        _, kr = lcx.rope_apply_qk(None, kd, cos, sin, pos0=k_pos0, out_dtype=odt)
+        o, lse = lcx.attn_fwd(qd, kr, vd, rope_q=True, cos=cos, sin=sin, rope=cfg, window=w.window,
+                              n_sink=w.n_sink, q_pos0=q_pos0, k_pos0=k_pos0, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _all(w, q, k, v, q_pos0=0, k_pos0=0):
+    B, Hq, n, d = q.shape
+    bb, hh, rr = np.meshgrid(np.arange(B), np.arange(Hq), np.arange(n), indexing="ij")
+    bb, hh, rr = bb.reshape(-1).astype(np.int32), hh.reshape(-1).astype(np.int32), rr.reshape(-1)
+    o_ref, l_ref = U.oracle_rows(w, q, k, v, bb, hh, rr, q_pos0=q_pos0, k_pos0=k_pos0)
+    return o_ref, l_ref
+
+
+@pytest.mark.parametrize("k_mode", ["pre_f16", "fused"])
+def test_tiny_workload_full(lcx, k_mode):
+    w = W.TINY
+    q, k, v = U.inputs(w)
+    o, lse = _run(lcx, w, q, k, v, k_mode=k_mode)
+    o_ref, l_ref = _all(w, q, k, v)
+    U.check(o.float().cpu().numpy().reshape(-1, w.d), lse.cpu().numpy().reshape(-1), o_ref, l_ref,
+            f"tiny/{k_mode}")
+
+
+SMALL = [
+    # name, Hq, Hkv, d, n, scheme, window, n_sink, B
+    ("n1", 4, 1, 64, 1, "ntk", -1, 0, 1),
+    ("n63", 4, 2, 128, 63, "plain", -1, 0, 1),
+    ("n65_d64", 8, 2, 64, 65, "yarn", -1, 0, 1),
+    ("n129", 2, 1, 128, 129, "pi", -1, 0, 1),
+    ("n333_b2", 4, 4, 128, 333, "ntk_parts", -1, 0, 2),
+    ("n700_gqa8", 8, 1, 128, 700, "dynamic_ntk", -1, 0, 1),
+    ("win_sink", 4, 1, 128, 900, "pi", 200, 4, 1),
+    ("win0_sink3", 2, 1, 64, 300, "ntk", 0, 3, 1),
+    ("win_big", 4, 2, 128, 520, "yarn", 64, 0, 1),
+    ("win_tiles", 4, 2, 64, 1000, "plain", 127, 70, 1),
+]
+
+
+@pytest.mark.parametrize("name,Hq,Hkv,d,n,scheme,window,n_sink,B", SMALL)
+def test_small_shapes_full(lcx, name, Hq, Hkv, d, n, scheme, window, n_sink, B):
+    w = W.Workload(name, B, Hq, Hkv, d, n, scheme, 10000.0 if d == 64 else 500000.0, 64, 256,
+                   cur_len=256, window=window, n_sink=n_sink, seed=100 + n)
+    q, k, v = U.inputs(w)
+    o_ref, l_ref = _all(w, q, k, v)
+    for k_mode in ("pre_f16", "fused"):
+        o, lse = _run(lcx, w, q, k, v, k_mode=k_mode)
+        U.check(o.float().cpu().numpy().reshape(-1, d), lse.cpu().numpy().reshape(-1), o_ref, l_ref,
+                f"{name}/{k_mode}")
+
+
+def test_f32_output_and_bf16_prerotated_k(lcx):
+    w = W.TINY.with_(n=300, seed=7)
+    q, k, v = U.inputs(w)
+    o_ref, l_ref = _all(w, q, k, v)
+    o, lse = _run(lcx, w, q, k, v, out_dtype=torch.float32)
+    e32 = U.check(o.cpu().numpy().reshape(-1, w.d), lse.cpu().numpy().reshape(-1), o_ref, l_ref, "f32-out")
+    # bf16 output rounding only adds ~2^-9 relative on top
+    assert e32[1] < 1e-3
+    o, lse = _run(lcx, w, q, k, v, k_mode="pre_bf16")
+    eo = np.abs(o.float().cpu().numpy().reshape(-1, w.d) - o_ref)
+    assert eo.max() <= U.O_MAX_ABS and eo.mean() <= U.O_MEAN_ABS
+
+
+def test_query_and_key_offsets_and_empty_rows(lcx):
+    # queries at positions 500.., keys at 300..; then keys entirely in the future
+    w = W.TINY.with_(seed=8)
+    q, _, _ = U.inputs(w, n_q=200)
+    _, k, v = U.inputs(w, n_kv=350)
+    o, lse = _run(lcx, w, q, k, v, q_pos0=500, k_pos0=300, tab_n=700)
+    bb = np.zeros(w.Hq * 200, np.int32)
+    hh = np.repeat(np.arange(w.Hq), 200).astype(np.int32)
+    rr = np.tile(np.arange(200), w.Hq)
+    o_ref, l_ref = U.oracle_rows(w, q, k, v, bb, hh, rr, q_pos0=500, k_pos0=300)
+    U.check(o.float().cpu().numpy().reshape(-1, w.d), lse.cpu().numpy().reshape(-1), o_ref, l_ref,
+            "offsets")
+    o, lse = _run(lcx, w, q, k, v, q_pos0=0, k_pos0=300, tab_n=700)
+    l = lse.cpu().numpy().reshape(-1)
+    o_np = o.float().cpu().numpy()
+    assert np.all(np.isneginf(l)) and np.all(o_np == 0)
+
+
+def test_peaky_softmax_exercises_rescaling(lcx):
+    # q scaled by 8 (still exact in bf16): logits ~ N(0, 64), the running max
+    # moves by far more than the lazy-rescale threshold
+    w = W.TINY.with_(n=600, seed=9)
+    q, k, v = U.inputs(w)
+    qf = (q.astype(np.uint32) << 16).view(np.float32) * 8.0
+    q8 = (qf.view(np.uint32) >> 16).astype(np.uint16)
+    o_ref, l_ref = _all(w, q8, k, v)
+    o, lse = _run(lcx, w, q8, k, v)
+    l_g = lse.cpu().numpy().reshape(-1)
+    eo = np.abs(o.float().cpu().numpy().reshape(-1, w.d) - o_ref)
+    el = np.abs(l_g - l_ref)
+    U.log(f"peaky: O max {eo.max():.3e} mean {eo.mean():.3e}, LSE max {el.max():.3e}")
+    assert eo.max() <= U.O_MAX_ABS and eo.mean() <= U.O_MEAN_ABS
+    # logits are 8x larger, so the same relative f16 rounding of q moves them
+    # (and the LSE, which follows the dominant key here) 8x more in absolute
+    # terms: error std ~2e-3 per row, so the max over 2400 rows sits near 5 sigma
+    assert el.max() <= 16 * U.LSE_MAX_ABS
+
+
+def test_deterministic_and_every_output_written(lcx):
+    w = W.TINY.with_(n=777, seed=10, Hq=8, Hkv=2, d=128, base=500000.0)
+    q, k, v = U.inputs(w)
+    qd, kd, vd = U.to_dev(q), U.to_dev(k), U.to_dev(v)
+    cfg = _cfg(lcx, w)
+    cos, sin = lcx.rope_tables(cfg, w.n, device=U.dev())
+    _, kr = lcx.rope_apply_qk(None, kd, cos, sin)
+    # outputs live inside NaN-filled guard bands
+    pad = 4096
+    big_o = torch.full((w.Hq * w.n * w.d + 2 * pad,), float("nan"), dtype=torch.bfloat16, device=U.dev())
+    big_l = torch.full((w.Hq * w.n + 2 * pad,), float("nan"), dtype=torch.float32, device=U.dev())
+    o = big_o[pad:pad + w.Hq * w.n * w.d].view(1, w.Hq, w.n, w.d)
+    l = big_l[pad:pad + w.Hq * w.n].view(1, w.Hq, w.n)
+    lcx.attn_fwd(qd, kr, vd, o, l, rope_q=True, cos=cos, sin=sin, rope=cfg)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any() and not torch.isnan(l).any()
+    assert torch.isnan(big_o[:pad]).all() and torch.isnan(big_o[-pad:]).all()
+    assert torch.isnan(big_l[:pad]).all() and torch.isnan(big_l[-pad:]).all()
+    o2, l2 = lcx.attn_fwd(qd, kr, vd, rope_q=True, cos=cos, sin=sin, rope=cfg)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(l, l2)
+
+
+def test_rope_tables_match_oracle(lcx):
+    for w in W.ALL:
+        cfg = _cfg(lcx, w)
+        th, pf, _ = U.oracle_freqs(w)
+        ranges = [(0, 2048), (max(0, w.n - 2048), w.n)]
+        rng = np.random.default_rng(1)
+        ranges += [(int(s), int(s) + 64) for s in rng.integers(0, w.n - 64, 16)]
+        worst = 0.0
+        for p0, p1 in ranges:
+            cos, sin = lcx.rope_tables(cfg, p1 - p0, pos0=p0, device=U.dev())
+            c_ref, s_ref = oracle.rope_table(th, w.d, pf, p0, p1 - p0)
+            torch.cuda.synchronize()
+            worst = max(worst, np.abs(cos.cpu().numpy() - c_ref).max(), np.abs(sin.cpu().numpy() - s_ref).max())
+        U.log(f"table {w.name}: max-abs {worst:.3e}")
+        assert worst <= U.TABLE_MAX_ABS
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float16, torch.bfloat16])
+def test_rope_apply_matches_oracle(lcx, out_dtype):
+    w = W.LLAMA8B_32K
+    n = 3000
+    q, k, _ = U.inputs(w, n_q=n, n_kv=n)
+    cfg = _cfg(lcx, w)
+    cos, sin = lcx.rope_tables(cfg, n + 5, device=U.dev())
+    qo, ko = lcx.rope_apply_qk(U.to_dev(q), U.to_dev(k), cos, sin, pos0=5, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    th, pf, _ = U.oracle_freqs(w)
+    ulp = 2.0 ** -11 if out_dtype == torch.float16 else 2.0 ** -8
+    for name, x, y in (("q", q, qo), ("k", k, ko)):
+        xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64).reshape(-1, w.d)
+        pos = np.tile(np.arange(n) + 5, x.shape[0] * x.shape[1])
+        ref = oracle.rope_rotate(xf, pos, th, pf)
+        got = y.float().cpu().numpy().reshape(-1, w.d)
+        err = np.abs(got - ref)
+        bound = ulp * np.abs(ref) * 1.01 + 1e-6 * np.abs(xf).sum(axis=1, keepdims=True) / 8 + 1e-7
+        U.log(f"rope apply {name} {out_dtype}: max-abs {err.max():.3e}")
+        assert np.all(err <= bound)
+    # in place in bf16
+    qd = U.to_dev(q)
+    ref_out, _ = lcx.rope_apply_qk(qd, None, cos, sin, pos0=5, out_dtype=torch.bfloat16)
+    lcx.rope_apply_qk(qd, None, cos, sin, pos0=5, q_out=qd, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(qd.view(torch.int16), ref_out.view(torch.int16))
+
+
+def test_merge_kernel_matches_oracle_merge(lcx):
+    rng = np.random.default_rng(2)
+    B, H, R, d = 2, 3, 777, 128
+    la = rng.normal(size=(B, H, R)) * 3
+    lb = rng.normal(size=(B, H, R)) * 3
+    la[0, 0, :50] = -np.inf
+    lb[0, 1, :50] = -np.inf
+    la[1, 2, :10] = lb[1, 2, :10] = -np.inf
+    oa = rng.normal(size=(B, H, R, d))
+    ob = rng.normal(size=(B, H, R, d))
+    oa[np.isneginf(la)] = 0
+    ob[np.isneginf(lb)] = 0
+    t = lambda a: torch.tensor(a, dtype=torch.float32, device=U.dev())
+    o_acc, l_acc, o_part, l_part = t(oa), t(la), t(ob), t(lb)
+    fin = torch.empty((B, H, R, d), dtype=torch.bfloat16, device=U.dev())
+    lcx.attn_merge(o_acc, l_acc, o_part, l_part, o_final=fin)
+    torch.cuda.synchronize()
+    oa32, ob32 = o_acc.new_tensor(oa).cpu().numpy(), o_part.cpu().numpy()
+    la32, lb32 = t(la).cpu().numpy(), l_part.cpu().numpy()
+    o_ref, l_ref = oracle.merge(np.stack([la32.reshape(-1), lb32.reshape(-1)]),
+                                np.stack([oa32.reshape(-1, d), ob32.reshape(-1, d)]))
+    l_g = l_acc.cpu().numpy().reshape(-1)
+    assert np.array_equal(np.isneginf(l_g), np.isneginf(l_ref))
+    fin_l = ~np.isneginf(l_ref)
+    assert np.abs(l_g[fin_l] - l_ref[fin_l]).max() < 1e-5
+    assert np.abs(o_acc.cpu().numpy().reshape(-1, d) - o_ref).max() < 1e-5
+    assert np.abs(fin.float().cpu().numpy().reshape(-1, d) - o_ref).max() < 2e-2
+
+
+@pytest.mark.parametrize("separate", [False, True])
+def test_chunked_driver_equals_oracle_and_one_shot(lcx, separate):
+    w = W.MILLION.with_(n=5000, chunk=1024, Hq=8, Hkv=2, seed=11)
+    q, k, v = U.inputs(w)
+    qd, kd, vd = U.to_dev(q), U.to_dev(k), U.to_dev(v)
+    cfg = _cfg(lcx, w)
+    cos, sin = lcx.rope_tables(cfg, w.n, device=U.dev())
+    _, kr = lcx.rope_apply_qk(None, kd, cos, sin)
+    acc_o = torch.empty((1, w.Hq, w.n, w.d), dtype=torch.float32, device=U.dev())
+    acc_l = torch.empty((1, w.Hq, w.n), dtype=torch.float32, device=U.dev())
+    part_o = torch.empty_like(acc_o) if separate else None
+    part_l = torch.empty_like(acc_l) if separate else None
+    o, lse = lcx.attn_fwd_chunked(qd, kr, vd, w.chunk, acc_o, acc_l, o_part=part_o, lse_part=part_l,
+                                  rope_q=True, cos=cos, sin=sin, rope=cfg)
+    o1, l1 = lcx.attn_fwd(qd, kr, vd, rope_q=True, cos=cos, sin=sin, rope=cfg, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    bb, hh, rr = U.sample_rows(w, 1500)
+    o_ref, l_ref = U.oracle_rows(w, q, k, v, bb, hh, rr)
+    U.check(o.float().cpu().numpy()[bb, hh, rr], lse.cpu().numpy()[bb, hh, rr], o_ref, l_ref,
+            f"chunked separate={separate}")
+    # chunked vs one call: P is rounded to bf16 against each chunk's own running
+    # max, so O differs at that rounding level; LSE comes from fp32 sums only
+    d_o = (acc_o - o1).abs()
+    assert d_o.max().item() < U.O_MAX_ABS and d_o.mean().item() < 1e-4
+    assert (acc_l - l1).abs().max().item() < 5e-5
+
+
+def test_accumulate_two_halves_equals_one_shot(lcx):
+    w = W.TINY.with_(n=1000, seed=12)
+    q, k, v = U.inputs(w)
+    qd, kd, vd = U.to_dev(q), U.to_dev(k), U.to_dev(v)
+    cfg = _cfg(lcx, w)
+    cos, sin = lcx.rope_tables(cfg, w.n, device=U.dev())
+    _, kr = lcx.rope_apply_qk(None, kd, cos, sin)
+    o_ref, l_ref = lcx.attn_fwd(qd, kr, vd, rope_q=True, cos=cos, sin=sin, rope=cfg,
+                                out_dtype=torch.float32)
+    # second half of the keys first, then the first half merged in the epilogue
+    half = 448
+    o, l = lcx.attn_fwd(qd, kr[:, :, half:], vd[:, :, half:], rope_q=True, cos=cos, sin=sin,
+                        rope=cfg, k_pos0=half, out_dtype=torch.float32)
+    lcx.attn_fwd(qd, kr[:, :, :half], vd[:, :, :half], o, l, rope_q=True, cos=cos, sin=sin,
+                 rope=cfg, accumulate=True)
+    torch.cuda.synchronize()
+    d_o = (o - o_ref).abs()
+    assert d_o.max().item() < U.O_MAX_ABS and d_o.mean().item() < 1e-4
+    assert (l - l_ref).abs().max().item() < 5e-5
