@@ -1,0 +1,211 @@
+"""Benchmark of the scaled-RoPE causal GQA attention path on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input that is
+already resident in HBM:
+  1. lcx_rope_freqs     frequencies (host, fp64) + cos/sin tables (GPU)
+  2. lcx_rope_apply_qk  K rotated once into f16
+  3. lcx_attn_fwd       causal GQA attention, RoPE fused into the Q load,
+                        O (bf16) + LSE (fp32)
+on the Llama-3-70B-shaped layer: B=1, 64 query / 8 KV heads, d=128,
+n=131072, dynamic NTK (base 500000, L_train 8192, l=131072).
+
+Prints ONE JSON line.  `value` is algorithmic causal-attention TFLOP/s of the
+whole step (4·d·Hq·n(n+1)/2 FLOP; masked work never counted).
+`roofline` is for the dominant kernel (attention), timed with HIP events on
+the stream it runs on.  `cpu_baseline` times the fp64 oracle on a bounded
+sample of rows of the same layer.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense bf16/f16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "causal attn TFLOP/s + % bf16 MFMA peak, 70B-shape GQA layer at 128K ctx"
+PMC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_llama3_70b_128k_pmc.json")
+KERNEL_SRC = os.path.join(ROOT, "long_context_attention_rope_amd", "csrc", "attn_fwd.hip")
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(launch_flop_bytes):
+    """HBM bytes per attention launch from the committed rocprofv3 counter runs,
+    only if they were taken on the current kernel source."""
+    try:
+        rec = json.load(open(PMC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, rows: int):
+    import numpy as np
+    import fixtures
+    import oracle
+    th, pf, lm = oracle.rope_freqs(w.scheme, w.base, w.d, w.L_train, w.L_target, w.cur_len,
+                                   w.alpha, w.beta)
+    rng = np.random.default_rng(12345)
+    heads = rng.integers(0, w.Hq, rows).astype(np.int32)
+    pos = rng.integers(0, w.n, rows).astype(np.int64)
+    flat = heads.astype(np.int64) * w.n + pos
+    q_rows = fixtures.rows_bf16(w.seed, fixtures.Q_ID, flat, w.d)
+    k = fixtures.normal_bf16(w.seed, fixtures.K_ID, (w.B, w.Hkv, w.n, w.d))
+    v = fixtures.normal_bf16(w.seed, fixtures.V_ID, (w.B, w.Hkv, w.n, w.d))
+    t0 = time.perf_counter()
+    oracle.attn_rows(q_rows, pos, heads, np.zeros(rows, np.int32), k, v, w.Hq, th, pf,
+                     lm / np.sqrt(w.d), True, w.window, w.n_sink)
+    dt = time.perf_counter() - t0
+    flop = 4 * w.d * int(np.sum(pos + 1))
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{rows} seeded rows (uniform head, uniform position) of the same layer, "
+                      f"fp64, {flop:.3e} algorithmic FLOP, K rotation of the needed heads included"}
+
+
+def copy_calibration(gib: float = 1.0, reps: int = 5):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    n = int(gib * (1 << 30)) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3_70b_128k_dynntk")
+    ap.add_argument("--k-mode", choices=["prerotate", "fused"], default="prerotate",
+                    help="K rotated once by lcx_rope_apply_qk (default) or inside the attention tile load")
+    ap.add_argument("--cpu-rows", type=int, default=2048, help="oracle rows for the CPU baseline (0: skip)")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(the path would shard by KV head group or by sequence ring, see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    import fixtures
+    import long_context_attention_rope_amd as lcx
+    from fixtures import workloads as W
+
+    w = W.BY_NAME[args.workload]
+    if w.chunk:
+        raise SystemExit("bench.py times single-call workloads; the chunked one is a parity case")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # synthetic inputs, generated on the host from the seeded generator, then resident in HBM
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q = to_dev(fixtures.normal_bf16(w.seed, fixtures.Q_ID, (w.B, w.Hq, w.n, w.d)))
+    k = to_dev(fixtures.normal_bf16(w.seed, fixtures.K_ID, (w.B, w.Hkv, w.n, w.d)))
+    v = to_dev(fixtures.normal_bf16(w.seed, fixtures.V_ID, (w.B, w.Hkv, w.n, w.d)))
+    cfg = lcx.rope_cfg(w.scheme, w.base, w.d, w.L_train, w.L_target, w.cur_len, w.alpha, w.beta)
+    half = w.d // 2
+    cos = torch.empty((w.n, half), dtype=torch.float32, device=dev)
+    sin = torch.empty((w.n, half), dtype=torch.float32, device=dev)
+    k_rot = torch.empty(k.shape, dtype=torch.float16, device=dev)
+    o = torch.empty((w.B, w.Hq, w.n, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.Hq, w.n), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        lcx.rope_freqs(cfg, cos, sin, 0)
+        if ev: ev[1].record(stream)
+        if args.k_mode == "prerotate":
+            lcx.rope_apply_qk(None, k, cos, sin, k_out=k_rot)
+            if ev: ev[2].record(stream)
+            lcx.attn_fwd(q, k_rot, v, o, lse, rope_q=True, cos=cos, sin=sin, rope=cfg,
+                         window=w.window, n_sink=w.n_sink)
+        else:
+            if ev: ev[2].record(stream)
+            lcx.attn_fwd(q, k, v, o, lse, rope_q=True, rope_k=True, cos=cos, sin=sin, rope=cfg,
+                         window=w.window, n_sink=w.n_sink)
+        if ev: ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    tab_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    rot_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    ms_step = wall * 1e3 / args.steps
+    flop = w.flop()
+    tokens = w.B * w.n
+    value = flop / (ms_step * 1e-3) / 1e12
+    attn_tflops = flop / (attn_ms * 1e-3) / 1e12
+    traffic = traffic_from_profile(flop)
+
+    tab_bytes = w.n * half * 8
+    rot_bytes = w.B * w.Hkv * w.n * w.d * 4 + tab_bytes
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": w.d, "seq_len": w.n, "rope": w.scheme, "rope_base": w.base,
+                   "L_train": w.L_train, "cur_len": w.cur_len, "causal": True,
+                   "k_rope": args.k_mode,
+                   "mfma": "QK^T f16 operands, PV bf16 operands, fp32 accumulate"},
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
+        "kernels_ms": {"rope_table": round(tab_ms, 4), "rope_apply_k": round(rot_ms, 4),
+                       "attn_fwd": round(attn_ms, 3)},
+        "hbm_gbs": {"rope_table": round(tab_bytes / (tab_ms * 1e-3) / 1e9, 1),
+                    "rope_apply_k": round(rot_bytes / (rot_ms * 1e-3) / 1e9, 1)
+                    if args.k_mode == "prerotate" else None},
+        "roofline": {"kernel": "attn_fwd", "bound": "mfma", "achieved": round(attn_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+    }
+    if args.cpu_rows > 0:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
