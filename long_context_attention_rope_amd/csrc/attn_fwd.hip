@@ -10,9 +10,8 @@
 // (window K_[i-w, i]) and §4.2 (sink tokens 0-3 always kept).
 //
 // Design (CDNA4, wave64):
-//  * Workgroup = 4 waves = 128 query rows of one head; each wave owns 32 rows.
-//    KV tiles of 64 keys are staged in LDS (double buffered, next tile's
-//    global loads in flight during the current tile's math).
+//  * Workgroup = NW waves; each wave owns 32 query rows of one head.  KV tiles
+//    of 64 keys are staged in LDS by the whole workgroup.
 //  * S^T = K·Q^T on v_mfma_f32_32x32x16_f16: the 32x32 accumulator of a wave
 //    puts all 32 scores of one query row (for a 32-key block) in lanes l and
 //    l^32, so row max / row sum are in-lane plus one permlane32 swap.
@@ -20,15 +19,20 @@
 //    operand of O^T += V^T·P^T on v_mfma_f32_32x32x16_bf16; V is transposed
 //    while being staged (key order permuted within each 16-key group to match
 //    the accumulator's row order), so each MFMA operand is one ds_read_b128.
+//  * Software pipeline across tiles: iteration t issues S(t+1) = K(t+1)·Q^T
+//    while the softmax of S(t) runs on the VALU, then O += V(t)·P(t).  K and V
+//    have their own double buffers (K two tiles ahead of use, V one), filled
+//    from registers loaded one iteration earlier through buffer loads whose
+//    range check zero-fills rows past the last key.  One barrier per tile.
 //  * Q is rotated (RoPE from the fp32 tables) once per workgroup in registers;
 //    K is either pre-rotated (f16) or rotated while being staged.
-//  * Rotated q/k are rounded once to f16 (8 more bits than bf16 where it
-//    matters: it keeps the LSE of short rows within 1e-3), P to bf16.
+//  * Rotated q/k are rounded once to f16 (three more mantissa bits than bf16:
+//    it keeps the LSE of short rows within 1e-3), P to bf16.
 //  * Online softmax in base 2 with the scale folded into one FMA; the O
 //    rescale is skipped while the running max grows by less than 2^8
 //    (exact: the final O/l uses the same reference max for both).
 //  * Tiles entirely outside the causal / window+sink mask are never visited;
-//    only tiles that straddle a mask edge are masked per element.
+//    only tiles that straddle a mask edge are masked per element (branch-free).
 //  * Block order: longest causal rows first; the G query heads of one KV head
 //    are dispatched consecutively to the same XCD so they share K/V in L2.
 #include "lcx_device.h"
@@ -38,22 +42,22 @@ namespace lcx {
 
 namespace {
 
-constexpr int NW = 4;          // waves per workgroup
-constexpr int BM = kBM;        // 128 query rows per workgroup
-constexpr int BN = kBN;        // 64 keys per tile
+constexpr int BN = kBN;           // 64 keys per tile
 constexpr float kLazyTau = 8.0f;  // log2 growth allowed before rescaling O
 
-template <int D>
+template <int D, int NW>
 struct Tile {
-  static constexpr int KSTR = D + 8;   // f16 elements per K row in LDS (pad: conflict-free reads)
-  static constexpr int VSTR = BN + 8;  // bf16 elements per V^T row in LDS
+  static constexpr int NT = 64 * NW;        // threads per workgroup
+  static constexpr int BM = 32 * NW;        // query rows per workgroup
+  static constexpr int KSTR = D + 8;        // f16 elements per K row in LDS (pad: conflict-free reads)
+  static constexpr int VSTR = BN + 8;       // bf16 elements per V^T row in LDS
   static constexpr int K_ELEMS = BN * KSTR;
   static constexpr int V_ELEMS = D * VSTR;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;  // uint16 elements per buffer
-  static constexpr int CPR = D / 8;                // 16-byte chunks per K row
-  static constexpr int KCH = BN * CPR / 256;       // K chunks per thread
-  static constexpr int KRSTEP = 256 / CPR;         // rows between a thread's chunks
-  static constexpr int DPT = D / 16;               // V d-values per thread (4 keys each)
+  static constexpr int CPR = D / 8;         // 16-byte chunks per K row
+  static constexpr int KCH = BN * CPR / NT; // K chunks per thread
+  static constexpr int KRSTEP = NT / CPR;   // rows between a thread's chunks
+  static constexpr int DPT = D / (4 * NW);  // V d-values per thread (for 4 keys)
+  static_assert(KCH >= 1 && DPT >= 2, "tile split");
 };
 
 // saturate a position difference to +-2^30: every comparison against a key
@@ -63,6 +67,11 @@ __device__ __forceinline__ int clamp_i32(int64_t x) {
 }
 __device__ __forceinline__ int clamp_tile(int64_t x) {
   return (int)(x < 0 ? 0 : (x > BN ? BN : x));
+}
+
+// Buffer resource over [base, base + bytes): lane offsets >= bytes read zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 // Q fragment for the B operand of S^T = K Q^T: lane (n, h2) holds
@@ -94,99 +103,154 @@ __device__ __forceinline__ void load_q(const AttnParams& p, const uint16_t* qbas
   }
 }
 
-template <int D, int KMODE>
-struct Stager {
-  using T = Tile<D>;
-  u32x4 kreg[T::KCH];
-  f32x4 kcos[KMODE == 2 ? T::KCH : 1];
-  f32x4 ksin[KMODE == 2 ? T::KCH : 1];
-  uint32_t vreg[4][T::DPT / 2];
+// K tile staging: global (buffer loads) -> registers -> LDS, row-major f16.
+// Per tile the resource starts at the tile's first key and ends at n_kv, so
+// rows past the last key read as zero; lane offsets are fixed for the loop.
+template <int D, int NW, int KMODE>
+struct KStager {
+  using T = Tile<D, NW>;
+  u32x4 reg[T::KCH];
+  f32x4 cs[KMODE == 2 ? T::KCH : 1];
+  f32x4 sn[KMODE == 2 ? T::KCH : 1];
+  const uint16_t* base;
+  const float* cb;
+  const float* sb;
+  int64_t rs;  // row stride, elements
+  int n_kv;
+  uint32_t off[T::KCH], toff[KMODE == 2 ? T::KCH : 1];
+  int lds_off[T::KCH];
 
-  // global -> registers for the tile starting at key j0
-  __device__ __forceinline__ void load(const AttnParams& p, const uint16_t* kbase,
-                                       const uint16_t* vbase, int64_t j0, int tid) {
+  __device__ __forceinline__ void init(const AttnParams& p, const uint16_t* kbase, int tid) {
+    base = kbase;
+    rs = p.ks_s;
+    n_kv = (int)p.n_kv;
     const int kc = tid % T::CPR;
     const int kr0 = tid / T::CPR;
 #pragma unroll
     for (int i = 0; i < T::KCH; ++i) {
-      const int64_t j = j0 + kr0 + i * T::KRSTEP;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      if (j < p.n_kv) z = *reinterpret_cast<const u32x4*>(kbase + j * p.ks_s + kc * 8);
-      kreg[i] = z;
-      if constexpr (KMODE == 2) {
-        f32x4 c1 = {1.f, 1.f, 1.f, 1.f}, s0 = {0.f, 0.f, 0.f, 0.f};
-        if (j < p.n_kv) {
-          const int64_t trow = p.k_pos0 + j - p.tab_pos0;
-          c1 = *reinterpret_cast<const f32x4*>(p.cos_tab + trow * (D / 2) + kc * 4);
-          s0 = *reinterpret_cast<const f32x4*>(p.sin_tab + trow * (D / 2) + kc * 4);
-        }
-        kcos[i] = c1;
-        ksin[i] = s0;
-      }
+      off[i] = (uint32_t)((kr0 + i * T::KRSTEP) * rs * 2) + (uint32_t)kc * 16u;
+      lds_off[i] = (kr0 + i * T::KRSTEP) * T::KSTR + kc * 8;
     }
-    const int vkg = tid & 15;
-    const int vdg = tid >> 4;
+    if constexpr (KMODE == 2) {
+      const int64_t r0 = p.k_pos0 - p.tab_pos0;  // table rows exist for keys 0 .. n_kv-1
+      cb = p.cos_tab + r0 * (D / 2);
+      sb = p.sin_tab + r0 * (D / 2);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t j = j0 + 4 * vkg + r;
-      const uint16_t* src = vbase + j * p.vs_s + vdg * T::DPT;
-      if constexpr (T::DPT == 8) {
-        u32x4 z = {0u, 0u, 0u, 0u};
-        if (j < p.n_kv) z = *reinterpret_cast<const u32x4*>(src);
+      for (int i = 0; i < T::KCH; ++i)
+        toff[i] = (uint32_t)(kr0 + i * T::KRSTEP) * (uint32_t)(D * 2) + (uint32_t)kc * 16u;
+    }
+  }
+  __device__ __forceinline__ void load(int j0) {
+    const uint32_t rows = (uint32_t)(n_kv - j0);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + j0 * rs, rows * (uint32_t)(rs * 2));
 #pragma unroll
-        for (int w = 0; w < 4; ++w) vreg[r][w] = z[w];
-      } else {
-        u32x2 z = {0u, 0u};
-        if (j < p.n_kv) z = *reinterpret_cast<const u32x2*>(src);
-        vreg[r][0] = z[0];
-        vreg[r][1] = z[1];
+    for (int i = 0; i < T::KCH; ++i) reg[i] = __builtin_amdgcn_raw_buffer_load_b128(r, off[i], 0, 0);
+    if constexpr (KMODE == 2) {
+      const __amdgpu_buffer_rsrc_t rc = make_rsrc(cb + j0 * (D / 2), rows * (uint32_t)(D * 2));
+      const __amdgpu_buffer_rsrc_t rsn = make_rsrc(sb + j0 * (D / 2), rows * (uint32_t)(D * 2));
+#pragma unroll
+      for (int i = 0; i < T::KCH; ++i) {
+        cs[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, toff[i], 0, 0));
+        sn[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsn, toff[i], 0, 0));
       }
     }
   }
-
-  // registers -> LDS stage buffer (K row-major f16, V transposed bf16)
-  __device__ __forceinline__ void store(uint16_t* stage, int tid) const {
-    const int kc = tid % T::CPR;
-    const int kr0 = tid / T::CPR;
-    uint16_t* ks = stage;
+  __device__ __forceinline__ void store(uint16_t* ks) const {
 #pragma unroll
     for (int i = 0; i < T::KCH; ++i) {
       u32x4 w;
       if constexpr (KMODE == 2)
-        w = rotate4_bf16<true>(kreg[i], kcos[i], ksin[i]);
+        w = rotate4_bf16<true>(reg[i], cs[i], sn[i]);
       else if constexpr (KMODE == 1)
-        w = bf16_to_f16_4(kreg[i]);
+        w = bf16_to_f16_4(reg[i]);
       else
-        w = kreg[i];
-      *reinterpret_cast<u32x4*>(ks + (kr0 + i * T::KRSTEP) * T::KSTR + kc * 8) = w;
-    }
-    // V^T: key group vkg (keys 4vkg..4vkg+3) goes to slot group perm(vkg % 4)
-    // of its 16-key chunk so that the 8 keys an MFMA lane needs are adjacent.
-    uint16_t* vt = stage + T::K_ELEMS;
-    const int vkg = tid & 15;
-    const int vdg = tid >> 4;
-    const int g4 = vkg & 3;
-    const int slot = 16 * (vkg >> 2) + 4 * ((g4 & 1) * 2 + (g4 >> 1));
-#pragma unroll
-    for (int e = 0; e < T::DPT; ++e) {
-      const int w = e >> 1;
-      uint32_t k0, k1, k2, k3;
-      if (e & 1) {
-        k0 = vreg[0][w] >> 16; k1 = vreg[1][w] >> 16; k2 = vreg[2][w] >> 16; k3 = vreg[3][w] >> 16;
-      } else {
-        k0 = vreg[0][w] & 0xffffu; k1 = vreg[1][w] & 0xffffu;
-        k2 = vreg[2][w] & 0xffffu; k3 = vreg[3][w] & 0xffffu;
-      }
-      u32x2 pk = {k0 | (k1 << 16), k2 | (k3 << 16)};
-      *reinterpret_cast<u32x2*>(vt + (vdg * T::DPT + e) * T::VSTR + slot) = pk;
+        w = reg[i];
+      *reinterpret_cast<u32x4*>(ks + lds_off[i]) = w;
     }
   }
 };
 
-template <int D, int KMODE>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
-  using T = Tile<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::STAGE];
+// V tile staging: each thread loads DPT d-values of 4 consecutive keys and
+// writes them transposed (V^T[d][key]); key group g of a 16-key chunk goes to
+// slot group (g&1)*2 + (g>>1) so that the 8 keys one MFMA lane needs are
+// adjacent (the accumulator row order of S^T).
+template <int D, int NW>
+struct VStager {
+  using T = Tile<D, NW>;
+  static constexpr int W = T::DPT / 2;  // 32-bit words per key
+  uint32_t reg[4][W];
+  const uint16_t* base;
+  int64_t rs;
+  int n_kv;
+  uint32_t off;
+  int lds_off;
+
+  __device__ __forceinline__ void init(const AttnParams& p, const uint16_t* vbase, int tid) {
+    base = vbase;
+    rs = p.vs_s;
+    n_kv = (int)p.n_kv;
+    const int vkg = tid & 15;
+    const int vdg = tid >> 4;
+    off = (uint32_t)((4 * vkg) * rs * 2) + (uint32_t)(vdg * T::DPT * 2);
+    const int g4 = vkg & 3;
+    lds_off = (vdg * T::DPT) * T::VSTR + 16 * (vkg >> 2) + 4 * ((g4 & 1) * 2 + (g4 >> 1));
+  }
+  __device__ __forceinline__ void load(int j0) {
+    const uint32_t rows = (uint32_t)(n_kv - j0);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + j0 * rs, rows * (uint32_t)(rs * 2));
+    const uint32_t rb = (uint32_t)(rs * 2);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if constexpr (W == 4) {
+        const u32x4 z = __builtin_amdgcn_raw_buffer_load_b128(r, off + k * rb, 0, 0);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) reg[k][w] = z[w];
+      } else if constexpr (W == 2) {
+        const u32x2 z = __builtin_amdgcn_raw_buffer_load_b64(r, off + k * rb, 0, 0);
+        reg[k][0] = z[0];
+        reg[k][1] = z[1];
+      } else {
+        reg[k][0] = __builtin_amdgcn_raw_buffer_load_b32(r, off + k * rb, 0, 0);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* vt) const {
+#pragma unroll
+    for (int e = 0; e < T::DPT; ++e) {
+      const int w = e >> 1;
+      // bytes {low half of key a, low half of key b} or the high halves
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      u32x2 pk = {__builtin_amdgcn_perm(reg[1][w], reg[0][w], sel),
+                  __builtin_amdgcn_perm(reg[3][w], reg[2][w], sel)};
+      *reinterpret_cast<u32x2*>(vt + lds_off + e * T::VSTR) = pk;
+    }
+  }
+};
+
+template <int D, int NW>
+__device__ __forceinline__ void qk_tile(const uint16_t* ks, const f16x8 (&qf)[D / 16], int l32, int h2,
+                                        f32x16 (&s)[2]) {
+  using T = Tile<D, NW>;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const f16x8 a = *reinterpret_cast<const f16x8*>(ks + (kb * 32 + l32) * T::KSTR + 16 * c + 8 * h2);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[c], s[kb], 0, 0, 0);
+    }
+  }
+}
+
+template <int D, int KMODE, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnParams p) {
+  using T = Tile<D, NW>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::K_ELEMS + 2 * T::V_ELEMS];
+  auto ks_buf = [&](int i) { return smem + i * T::K_ELEMS; };
+  auto vs_buf = [&](int i) { return smem + 2 * T::K_ELEMS + i * T::V_ELEMS; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -217,7 +281,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
   const uint16_t* kbase = p.k + b * p.ks_b + hkv * p.ks_h;
   const uint16_t* vbase = p.v + b * p.vs_b + hkv * p.vs_h;
 
-  const int64_t row0 = (int64_t)qblk * BM;
+  const int64_t row0 = (int64_t)qblk * T::BM;
   const int64_t wrow0 = row0 + wave * 32;
   const int64_t qi = wrow0 + l32;  // this lane's query row
   const int64_t qpos = p.q_pos0 + qi;
@@ -226,8 +290,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
   f16x8 qf[D / 16];
   load_q<D>(p, qbase, qi, h2, qf);
 
-  // ---- KV tile range for the whole block
-  const int64_t blk_last = (row0 + BM < p.n_q ? row0 + BM : p.n_q) - 1;
+  // ---- KV tile range for the whole block: optional sink tiles, then the
+  // window / causal range
+  const int64_t blk_last = (row0 + T::BM < p.n_q ? row0 + T::BM : p.n_q) - 1;
   const int64_t qpos_min = p.q_pos0 + row0;
   const int64_t qpos_max = p.q_pos0 + blk_last;
   int64_t j_hi = p.n_kv;
@@ -250,7 +315,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
     if (sink_t1 > win_t0) sink_t1 = win_t0;
   }
   if (win_t1 < win_t0) win_t1 = win_t0;
-  const int64_t n_tiles = sink_t1 + (win_t1 - win_t0);
+  const int sink_n = (int)sink_t1;
+  const int win_0 = (int)win_t0;
+  const int ntl = (int)(sink_t1 + (win_t1 - win_t0));
+  auto tile_j0 = [&](int t) { return (t < sink_n ? t : win_0 + (t - sink_n)) * BN; };
 
   // ---- per-lane softmax state (row qi; lanes l and l^32 share the row)
   f32x16 oacc[D / 32];
@@ -265,39 +333,33 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
   const int64_t wqpos_min = p.q_pos0 + wrow0;
   const int64_t wqpos_max = p.q_pos0 + (wq_last >= wrow0 ? wq_last : wrow0);
 
-  Stager<D, KMODE> st;
-  if (n_tiles > 0) {
-    const int64_t j0 = (0 < sink_t1 ? 0 : win_t0) * BN;
-    st.load(p, kbase, vbase, j0, tid);
-    st.store(smem, tid);
+  KStager<D, NW, KMODE> kst;
+  VStager<D, NW> vst;
+  kst.init(p, kbase, tid);
+  vst.init(p, vbase, tid);
+
+  // ---- prologue: tile 0 in LDS buffer 0
+  if (ntl > 0) {
+    kst.load(tile_j0(0));
+    vst.load(tile_j0(0));
+    kst.store(ks_buf(0));
+    vst.store(vs_buf(0));
   }
   __syncthreads();
 
-  for (int64_t it = 0; it < n_tiles; ++it) {
-    const int64_t tile = it < sink_t1 ? it : win_t0 + (it - sink_t1);
-    const int64_t j0 = tile * BN;
-    const uint16_t* stage = smem + (it & 1) * T::STAGE;
-    const bool has_next = it + 1 < n_tiles;
-    if (has_next) {
-      const int64_t nt = (it + 1) < sink_t1 ? (it + 1) : win_t0 + (it + 1 - sink_t1);
-      st.load(p, kbase, vbase, nt * BN, tid);
+  for (int t = 0; t < ntl; ++t) {
+    const int j0 = tile_j0(t);
+    // next tile's global loads are in flight during this tile's math
+    if (t + 1 < ntl) {
+      kst.load(tile_j0(t + 1));
+      vst.load(tile_j0(t + 1));
     }
 
-    // ---- S^T = K Q^T for two 32-key blocks
-    f32x16 sacc[2];
-    const uint16_t* ks = stage;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        const f16x8 a = *reinterpret_cast<const f16x8*>(ks + (kb * 32 + l32) * T::KSTR + 16 * c + 8 * h2);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[c], sacc[kb], 0, 0, 0);
-      }
-    }
+    // ---- S(t) = K(t) Q^T
+    f32x16 s_cur[2];
+    qk_tile<D, NW>(ks_buf(t & 1), qf, l32, h2, s_cur);
 
-    // ---- mask (only for tiles that straddle a mask edge for this wave)
+    // ---- mask S(t) (only for tiles that straddle a mask edge for this wave)
     const int64_t kpos_min = p.k_pos0 + j0;
     const int64_t kpos_max = p.k_pos0 + (j0 + BN <= p.n_kv ? j0 + BN : p.n_kv) - 1;
     const bool all_kept = (j0 + BN <= p.n_kv) && (!p.causal || kpos_max <= wqpos_min) &&
@@ -318,16 +380,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
         for (int r = 0; r < 16; ++r) {
           const int off = kb * 32 + (r >> 2) * 8 + h2 * 4 + (r & 3);
           const bool ok = (off < krem) & (off <= hi) & ((off >= lo) | (off < srem));
-          sacc[kb][r] = ok ? sacc[kb][r] : -INFINITY;
+          s_cur[kb][r] = ok ? s_cur[kb][r] : -INFINITY;
         }
     }
 
-    // ---- online softmax (base 2)
+    // ---- online softmax of S(t) (base 2)
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kb][r]);
     mx = xor32_max(mx) * p.scale_log2;
     const float m_new = fmaxf(m_run, mx);
     if (__any(m_new > m_run + kLazyTau)) {
@@ -346,7 +408,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
       float pv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], p.scale_log2, -m_use));
+        pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][r], p.scale_log2, -m_use));
         l_run += pv[r];
       }
 #pragma unroll
@@ -358,8 +420,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
       }
     }
 
-    // ---- O^T += V^T P^T
-    const uint16_t* vt = stage + T::K_ELEMS;
+    // ---- O^T += V(t)^T P^T
+    const uint16_t* vt = vs_buf(t & 1);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -369,7 +431,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
       }
     }
 
-    if (has_next) st.store(smem + ((it + 1) & 1) * T::STAGE, tid);
+    // ---- stage tile t+1 into the other buffer (last read before the
+    // previous barrier)
+    if (t + 1 < ntl) {
+      kst.store(ks_buf((t + 1) & 1));
+      vst.store(vs_buf((t + 1) & 1));
+    }
     __syncthreads();
   }
 
@@ -435,27 +502,31 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
   }
 }
 
-template <int D>
-hipError_t launch_d(const AttnParams& p, hipStream_t s, unsigned grid) {
+template <int D, int NW>
+hipError_t launch_dn(const AttnParams& p, hipStream_t s, unsigned grid) {
+  const dim3 block(64 * NW);
   switch (p.k_mode) {
-    case 0: hipLaunchKernelGGL((attn_fwd_kernel<D, 0>), dim3(grid), dim3(256), 0, s, p); break;
-    case 1: hipLaunchKernelGGL((attn_fwd_kernel<D, 1>), dim3(grid), dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL((attn_fwd_kernel<D, 2>), dim3(grid), dim3(256), 0, s, p); break;
+    case 0: hipLaunchKernelGGL((attn_fwd_kernel<D, 0, NW>), dim3(grid), block, 0, s, p); break;
+    case 1: hipLaunchKernelGGL((attn_fwd_kernel<D, 1, NW>), dim3(grid), block, 0, s, p); break;
+    default: hipLaunchKernelGGL((attn_fwd_kernel<D, 2, NW>), dim3(grid), block, 0, s, p); break;
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
+int attn_rows_per_block(int d) { return 32 * (d == 64 ? kNWd64 : kNWd128); }
+
 hipError_t launch_attn_fwd(const AttnParams& p_in, hipStream_t s) {
   AttnParams p = p_in;
-  p.n_qblk = (int32_t)((p.n_q + BM - 1) / BM);
+  const int bm = attn_rows_per_block(p.d);
+  p.n_qblk = (int32_t)((p.n_q + bm - 1) / bm);
   const int64_t units = (int64_t)p.B * p.Hkv * p.n_qblk;
   p.xcd_map = (units % 8 == 0) ? 1 : 0;
   const int64_t grid = units * p.G;
   if (grid == 0) return hipSuccess;
-  if (p.d == 64) return launch_d<64>(p, s, (unsigned)grid);
-  return launch_d<128>(p, s, (unsigned)grid);
+  if (p.d == 64) return launch_dn<64, kNWd64>(p, s, (unsigned)grid);
+  return launch_dn<128, kNWd128>(p, s, (unsigned)grid);
 }
 
 }  // namespace lcx

@@ -154,7 +154,13 @@ lcx_status check_attn(const lcx_attn_args* a, bool chunked) {
     return fail(LCX_ERR_UNSUPPORTED, "o strides must keep rows 16-byte aligned");
   if (a->lse_strides[0] < 0 || a->lse_strides[1] < 0)
     return fail(LCX_ERR_INVALID_ARG, "lse strides must be >= 0");
-  const int64_t nqblk = (a->n_q + lcx::kBM - 1) / lcx::kBM;
+  // the kernel addresses one KV head's keys with 32-bit buffer offsets
+  const int64_t lim = (int64_t)1 << 31;
+  if (a->n_kv * a->k_strides[2] * 2 >= lim || a->n_kv * a->v_strides[2] * 2 >= lim ||
+      (a->rope_k && a->n_kv * a->d * 2 >= lim))
+    return fail(LCX_ERR_UNSUPPORTED, "one KV head spans 2 GiB or more (split the keys into chunks)");
+  const int bm = lcx::attn_rows_per_block(a->d);
+  const int64_t nqblk = (a->n_q + bm - 1) / bm;
   if ((int64_t)a->B * a->Hq * nqblk >= (int64_t)1 << 31)
     return fail(LCX_ERR_UNSUPPORTED, "problem too large for one launch");
   return LCX_OK;

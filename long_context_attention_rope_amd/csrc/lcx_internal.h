@@ -90,7 +90,9 @@ hipError_t launch_finalize(const float* o_acc, const float* lse_acc, void* o, in
                            const int64_t o_st[3], const int64_t lse_st[2], hipStream_t s);
 
 // attention tiling (shared by the launcher and the host-side validation)
-constexpr int kBM = 128;  // query rows per workgroup (4 waves x 32)
-constexpr int kBN = 64;   // keys per KV tile
+constexpr int kBN = 64;      // keys per KV tile
+constexpr int kNWd64 = 4;    // waves (32 query rows each) per workgroup, d = 64
+constexpr int kNWd128 = 8;   // d = 128
+int attn_rows_per_block(int d);
 
 }  // namespace lcx
