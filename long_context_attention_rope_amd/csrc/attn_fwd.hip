@@ -19,11 +19,11 @@
 //    operand of O^T += V^T·P^T on v_mfma_f32_32x32x16_bf16; V is transposed
 //    while being staged (key order permuted within each 16-key group to match
 //    the accumulator's row order), so each MFMA operand is one ds_read_b128.
-//  * Software pipeline across tiles: iteration t issues S(t+1) = K(t+1)·Q^T
-//    while the softmax of S(t) runs on the VALU, then O += V(t)·P(t).  K and V
-//    have their own double buffers (K two tiles ahead of use, V one), filled
-//    from registers loaded one iteration earlier through buffer loads whose
-//    range check zero-fills rows past the last key.  One barrier per tile.
+//  * Per tile: S(t) = K(t)·Q^T, softmax, O += V(t)·P(t), with tile t+1's
+//    buffer loads in flight (their range check zero-fills rows past the last
+//    key) and staged into the other LDS buffer at the end; one barrier per
+//    tile.  For d = 128 a workgroup is 8 waves (256 rows) and two waves share
+//    each SIMD, so one wave's softmax overlaps the other's MFMAs.
 //  * Q is rotated (RoPE from the fp32 tables) once per workgroup in registers;
 //    K is either pre-rotated (f16) or rotated while being staged.
 //  * Rotated q/k are rounded once to f16 (three more mantissa bits than bf16:
@@ -141,7 +141,7 @@ struct KStager {
     }
   }
   __device__ __forceinline__ void load(int j0) {
-    const uint32_t rows = (uint32_t)(n_kv - j0);
+    const uint32_t rows = n_kv > j0 ? (uint32_t)(n_kv - j0) : 0u;  // tiles past the end: empty range
     const __amdgpu_buffer_rsrc_t r = make_rsrc(base + j0 * rs, rows * (uint32_t)(rs * 2));
 #pragma unroll
     for (int i = 0; i < T::KCH; ++i) reg[i] = __builtin_amdgcn_raw_buffer_load_b128(r, off[i], 0, 0);
@@ -196,7 +196,7 @@ struct VStager {
     lds_off = (vdg * T::DPT) * T::VSTR + 16 * (vkg >> 2) + 4 * ((g4 & 1) * 2 + (g4 >> 1));
   }
   __device__ __forceinline__ void load(int j0) {
-    const uint32_t rows = (uint32_t)(n_kv - j0);
+    const uint32_t rows = n_kv > j0 ? (uint32_t)(n_kv - j0) : 0u;  // tiles past the end: empty range
     const __amdgpu_buffer_rsrc_t r = make_rsrc(base + j0 * rs, rows * (uint32_t)(rs * 2));
     const uint32_t rb = (uint32_t)(rs * 2);
 #pragma unroll
@@ -338,28 +338,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
   kst.init(p, kbase, tid);
   vst.init(p, vbase, tid);
 
-  // ---- prologue: tile 0 in LDS buffer 0
-  if (ntl > 0) {
-    kst.load(tile_j0(0));
-    vst.load(tile_j0(0));
-    kst.store(ks_buf(0));
-    vst.store(vs_buf(0));
-  }
-  __syncthreads();
-
-  for (int t = 0; t < ntl; ++t) {
-    const int j0 = tile_j0(t);
-    // next tile's global loads are in flight during this tile's math
-    if (t + 1 < ntl) {
-      kst.load(tile_j0(t + 1));
-      vst.load(tile_j0(t + 1));
-    }
-
-    // ---- S(t) = K(t) Q^T
-    f32x16 s_cur[2];
-    qk_tile<D, NW>(ks_buf(t & 1), qf, l32, h2, s_cur);
-
-    // ---- mask S(t) (only for tiles that straddle a mask edge for this wave)
+  // ---- per-tile pieces of the online softmax
+  // mask S(t) (only for tiles that straddle a mask edge for this wave)
+  auto mask_tile = [&](f32x16 (&s)[2], const int j0) {
     const int64_t kpos_min = p.k_pos0 + j0;
     const int64_t kpos_max = p.k_pos0 + (j0 + BN <= p.n_kv ? j0 + BN : p.n_kv) - 1;
     const bool all_kept = (j0 + BN <= p.n_kv) && (!p.causal || kpos_max <= wqpos_min) &&
@@ -380,17 +361,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
         for (int r = 0; r < 16; ++r) {
           const int off = kb * 32 + (r >> 2) * 8 + h2 * 4 + (r & 3);
           const bool ok = (off < krem) & (off <= hi) & ((off >= lo) | (off < srem));
-          s_cur[kb][r] = ok ? s_cur[kb][r] : -INFINITY;
+          s[kb][r] = ok ? s[kb][r] : -INFINITY;
         }
     }
-
-    // ---- online softmax of S(t) (base 2)
+  };
+  // row max of a score tile, in scaled log2 units, shared by lanes l and l^32
+  auto tile_max = [&](const f32x16 (&s)[2]) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kb][r]);
-    mx = xor32_max(mx) * p.scale_log2;
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    return xor32_max(mx) * p.scale_log2;
+  };
+  // move the reference max when the row max grew by more than 2^kLazyTau
+  auto rescale = [&](const float mx) {
     const float m_new = fmaxf(m_run, mx);
     if (__any(m_new > m_run + kLazyTau)) {
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -401,6 +386,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
     }
+  };
+  // P = exp2(S·scale - m) in bf16, row sums, O^T += V^T P^T
+  auto exp_pv = [&](const f32x16 (&s)[2], const uint16_t* vt) {
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     bf16x8 pf[4];
 #pragma unroll
@@ -408,7 +396,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
       float pv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][r], p.scale_log2, -m_use));
+        pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], p.scale_log2, -m_use));
         l_run += pv[r];
       }
 #pragma unroll
@@ -419,9 +407,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
         pf[kb * 2 + hlf] = __builtin_bit_cast(bf16x8, w);
       }
     }
-
-    // ---- O^T += V(t)^T P^T
-    const uint16_t* vt = vs_buf(t & 1);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -430,14 +415,34 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kc], oacc[db], 0, 0, 0);
       }
     }
+  };
 
-    // ---- stage tile t+1 into the other buffer (last read before the
-    // previous barrier)
-    if (t + 1 < ntl) {
-      kst.store(ks_buf((t + 1) & 1));
-      vst.store(vs_buf((t + 1) & 1));
+  {
+    // ---- one tile at a time: S(t), softmax, PV; tile t+1's global loads in
+    // flight meanwhile, staged into the other buffer at the end
+    if (ntl > 0) {
+      kst.load(tile_j0(0));
+      vst.load(tile_j0(0));
+      kst.store(ks_buf(0));
+      vst.store(vs_buf(0));
     }
     __syncthreads();
+    for (int t = 0; t < ntl; ++t) {
+      if (t + 1 < ntl) {
+        kst.load(tile_j0(t + 1));
+        vst.load(tile_j0(t + 1));
+      }
+      f32x16 s_cur[2];
+      qk_tile<D, NW>(ks_buf(t & 1), qf, l32, h2, s_cur);
+      mask_tile(s_cur, tile_j0(t));
+      rescale(tile_max(s_cur));
+      exp_pv(s_cur, vs_buf(t & 1));
+      if (t + 1 < ntl) {  // the other buffer was last read before the previous barrier
+        kst.store(ks_buf((t + 1) & 1));
+        vst.store(vs_buf((t + 1) & 1));
+      }
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: O = O_acc / l, LSE = ln 2 · (m + log2 l)
