@@ -96,6 +96,8 @@ def main():
                     help="K rotated once by lcx_rope_apply_qk (default) or inside the attention tile load")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="oracle rows for the CPU baseline (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-merge-check", dest="merge_check", action="store_false",
+                    help="skip timing the merge pass on this layer's partial sizes")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -160,6 +162,27 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # the merge pass (chunked / ring form) on partials of this layer's size, timed
+    # on its own after the step loop: reads two fp32 (O, LSE), writes one
+    merge_gbs = None
+    if args.merge_check:
+        del o, k_rot
+        oa = torch.zeros((w.B, w.Hq, w.n, w.d), dtype=torch.float32, device=dev)
+        ob = torch.zeros_like(oa)
+        la = torch.zeros((w.B, w.Hq, w.n), dtype=torch.float32, device=dev)
+        lb = torch.zeros_like(la)
+        lcx.attn_merge(oa, la, ob, lb)
+        m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        m0.record(stream)
+        for _ in range(3):
+            lcx.attn_merge(oa, la, ob, lb)
+        m1.record(stream)
+        torch.cuda.synchronize()
+        merge_ms = m0.elapsed_time(m1) / 3
+        merge_bytes = 3 * (oa.numel() + la.numel()) * 4
+        merge_gbs = round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1)
+        del oa, ob, la, lb
+
     tab_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     rot_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
@@ -197,7 +220,8 @@ def main():
                        "attn_fwd": round(attn_ms, 3)},
         "hbm_gbs": {"rope_table": round(tab_bytes / (tab_ms * 1e-3) / 1e9, 1),
                     "rope_apply_k": round(rot_bytes / (rot_ms * 1e-3) / 1e9, 1)
-                    if args.k_mode == "prerotate" else None},
+                    if args.k_mode == "prerotate" else None,
+                    "attn_merge": merge_gbs, "peak": PEAK_HBM_GBS},
         "roofline": {"kernel": "attn_fwd", "bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
