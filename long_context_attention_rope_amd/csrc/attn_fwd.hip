@@ -45,20 +45,54 @@ namespace {
 constexpr int BN = kBN;           // 64 keys per tile
 constexpr float kLazyTau = 8.0f;  // log2 growth allowed before rescaling O
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
 template <int D, int NW>
 struct Tile {
-  static constexpr int NT = 64 * NW;        // threads per workgroup
-  static constexpr int BM = 32 * NW;        // query rows per workgroup
-  static constexpr int KSTR = D + 8;        // f16 elements per K row in LDS (pad: conflict-free reads)
-  static constexpr int VSTR = BN + 8;       // bf16 elements per V^T row in LDS
-  static constexpr int K_ELEMS = BN * KSTR;
-  static constexpr int V_ELEMS = D * VSTR;
-  static constexpr int CPR = D / 8;         // 16-byte chunks per K row
-  static constexpr int KCH = BN * CPR / NT; // K chunks per thread
-  static constexpr int KRSTEP = NT / CPR;   // rows between a thread's chunks
-  static constexpr int DPT = D / (4 * NW);  // V d-values per thread (for 4 keys)
-  static_assert(KCH >= 1 && DPT >= 2, "tile split");
+  static constexpr int NT = 64 * NW;          // threads per workgroup
+  static constexpr int BM = 32 * NW;          // query rows per workgroup
+  static constexpr int CPR = D / 8;           // 16-byte chunks per K / V row
+  static constexpr int ELEMS = BN * D;        // 16-bit elements per K or V tile in LDS
+  static constexpr int RPL = 1024 / (2 * D);  // rows per wave-wide LDS load (64 lanes x 16 B)
+  static constexpr int LPW = BN / RPL / NW;   // such loads per wave per tile
+  static constexpr int KCH = BN * CPR / NT;   // K chunks per thread (register staging)
+  static constexpr int KRSTEP = NT / CPR;     // rows between a thread's chunks
+  static_assert(LPW >= 1 && BN % (RPL * NW) == 0 && KCH >= 1, "tile split");
 };
+
+// LDS layout of a K or V tile: row r (key j0 + r) is 2D bytes, unpadded, with
+// its 16-byte chunk c stored in slot c ^ swz(r).  The QK^T operand reads take
+// one chunk of 16 consecutive rows per 16 lanes; the transposing PV operand
+// reads take 4 chunks of 4 consecutive rows per 32 lanes.  Each swizzle puts
+// those chunks in distinct 16-byte bank groups of the 256-byte bank line.
+template <int D>
+__device__ __forceinline__ int k_swz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int r) {
+  return D == 128 ? ((4 * (r & 3)) ^ (2 * ((r >> 2) & 1)))
+                  : ((4 * ((r >> 1) & 1)) ^ (2 * ((r >> 2) & 1)));
+}
+
+// s_waitcnt immediate (gfx9 encoding) that waits for all but n vector memory
+// operations and nothing else
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Workgroup barrier between tile steps.  Before it this wave's LDS reads have
+// returned (lgkmcnt 0) and all but its newest `n_vm` vector memory ops (the
+// copy of a later tile) have landed; the compiler-only fences keep every
+// memory access on its side.  __syncthreads() would also drain the copies
+// still in flight.
+template <int N_VM>
+__device__ __forceinline__ void stage_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(N_VM) & ~(15 << 8));
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // saturate a position difference to +-2^30: every comparison against a key
 // offset in [0, BN) keeps its outcome
@@ -103,11 +137,70 @@ __device__ __forceinline__ void load_q(const AttnParams& p, const uint16_t* qbas
   }
 }
 
-// K tile staging: global (buffer loads) -> registers -> LDS, row-major f16.
-// Per tile the resource starts at the tile's first key and ends at n_kv, so
-// rows past the last key read as zero; lane offsets are fixed for the loop.
+// One buffer load of 16 bytes per lane straight into LDS: lane L's bytes land
+// at LDS address lds_addr + 16 L (lds_addr wave-uniform, through M0).  Written
+// as an asm block rather than the compiler builtin so that the compiler does
+// not track it: with the builtin it put waits for the copy just issued in
+// front of the reads of an unrelated stage in one of the unrolled steps.  The
+// kernels wait for these copies themselves (vmcnt in stage_barrier).  Nothing
+// else in these kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
+                                           uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(rsrc), "s"(lds_addr)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Tile copy global -> LDS with no register round trip: per wave LPW buffer
+// loads of 64 lanes x 16 bytes, each filling RPL consecutive LDS rows; lane L
+// of load i fills row r = (wave·LPW + i)·RPL + L / CPR, slot L % CPR, with
+// the row's chunk (L % CPR) ^ swz(r).  The resource starts at the tile's first
+// key and ends at the last key, so rows past the end land as zeros.
+template <int D, int NW, bool K_SWZ>
+struct LdsCopy {
+  using T = Tile<D, NW>;
+  const uint16_t* base;
+  int64_t rs;  // row stride, elements
+  int n_kv;
+  int row0;    // first LDS row of this wave (wave-uniform)
+  uint32_t off[T::LPW];
+
+  __device__ __forceinline__ void init(const uint16_t* b, int64_t stride, int64_t nkv, int wave,
+                                       int lane) {
+    base = b;
+    rs = stride;
+    n_kv = (int)nkv;
+    row0 = wave * T::LPW * T::RPL;
+#pragma unroll
+    for (int i = 0; i < T::LPW; ++i) {
+      const int r = row0 + i * T::RPL + lane / T::CPR;
+      const int c = (lane % T::CPR) ^ (K_SWZ ? k_swz<D>(r) : v_swz<D>(r));
+      off[i] = (uint32_t)(r * rs * 2) + (uint32_t)c * 16u;
+    }
+  }
+  __device__ __forceinline__ void issue(uint16_t* lds, int j0) const {
+    const uint32_t rows = n_kv > j0 ? (uint32_t)(n_kv - j0) : 0u;  // tiles past the end: empty range
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + j0 * rs, rows * (uint32_t)(rs * 2));
+#pragma unroll
+    for (int i = 0; i < T::LPW; ++i) {
+      const uint32_t la = (uint32_t)(uintptr_t)(lds_void*)(lds + (row0 + i * T::RPL) * D);
+      lds_copy16(r, off[i], __builtin_amdgcn_readfirstlane(la));
+    }
+  }
+};
+
+// K staging through registers for K that is converted on the way (bf16 -> f16,
+// or rotated from the fp32 tables): global (buffer loads) -> registers -> LDS
+// in the swizzled layout above.
 template <int D, int NW, int KMODE>
-struct KStager {
+struct KRegStage {
   using T = Tile<D, NW>;
   u32x4 reg[T::KCH];
   f32x4 cs[KMODE == 2 ? T::KCH : 1];
@@ -128,8 +221,9 @@ struct KStager {
     const int kr0 = tid / T::CPR;
 #pragma unroll
     for (int i = 0; i < T::KCH; ++i) {
-      off[i] = (uint32_t)((kr0 + i * T::KRSTEP) * rs * 2) + (uint32_t)kc * 16u;
-      lds_off[i] = (kr0 + i * T::KRSTEP) * T::KSTR + kc * 8;
+      const int r = kr0 + i * T::KRSTEP;
+      off[i] = (uint32_t)(r * rs * 2) + (uint32_t)kc * 16u;
+      lds_off[i] = r * D + 8 * (kc ^ k_swz<D>(r));
     }
     if constexpr (KMODE == 2) {
       const int64_t r0 = p.k_pos0 - p.tab_pos0;  // table rows exist for keys 0 .. n_kv-1
@@ -161,76 +255,18 @@ struct KStager {
       u32x4 w;
       if constexpr (KMODE == 2)
         w = rotate4_bf16<true>(reg[i], cs[i], sn[i]);
-      else if constexpr (KMODE == 1)
-        w = bf16_to_f16_4(reg[i]);
       else
-        w = reg[i];
+        w = bf16_to_f16_4(reg[i]);
       *reinterpret_cast<u32x4*>(ks + lds_off[i]) = w;
     }
   }
 };
 
-// V tile staging: each thread loads DPT d-values of 4 consecutive keys and
-// writes them transposed (V^T[d][key]); key group g of a 16-key chunk goes to
-// slot group (g&1)*2 + (g>>1) so that the 8 keys one MFMA lane needs are
-// adjacent (the accumulator row order of S^T).
-template <int D, int NW>
-struct VStager {
-  using T = Tile<D, NW>;
-  static constexpr int W = T::DPT / 2;  // 32-bit words per key
-  uint32_t reg[4][W];
-  const uint16_t* base;
-  int64_t rs;
-  int n_kv;
-  uint32_t off;
-  int lds_off;
-
-  __device__ __forceinline__ void init(const AttnParams& p, const uint16_t* vbase, int tid) {
-    base = vbase;
-    rs = p.vs_s;
-    n_kv = (int)p.n_kv;
-    const int vkg = tid & 15;
-    const int vdg = tid >> 4;
-    off = (uint32_t)((4 * vkg) * rs * 2) + (uint32_t)(vdg * T::DPT * 2);
-    const int g4 = vkg & 3;
-    lds_off = (vdg * T::DPT) * T::VSTR + 16 * (vkg >> 2) + 4 * ((g4 & 1) * 2 + (g4 >> 1));
-  }
-  __device__ __forceinline__ void load(int j0) {
-    const uint32_t rows = n_kv > j0 ? (uint32_t)(n_kv - j0) : 0u;  // tiles past the end: empty range
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + j0 * rs, rows * (uint32_t)(rs * 2));
-    const uint32_t rb = (uint32_t)(rs * 2);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if constexpr (W == 4) {
-        const u32x4 z = __builtin_amdgcn_raw_buffer_load_b128(r, off + k * rb, 0, 0);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) reg[k][w] = z[w];
-      } else if constexpr (W == 2) {
-        const u32x2 z = __builtin_amdgcn_raw_buffer_load_b64(r, off + k * rb, 0, 0);
-        reg[k][0] = z[0];
-        reg[k][1] = z[1];
-      } else {
-        reg[k][0] = __builtin_amdgcn_raw_buffer_load_b32(r, off + k * rb, 0, 0);
-      }
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* vt) const {
-#pragma unroll
-    for (int e = 0; e < T::DPT; ++e) {
-      const int w = e >> 1;
-      // bytes {low half of key a, low half of key b} or the high halves
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      u32x2 pk = {__builtin_amdgcn_perm(reg[1][w], reg[0][w], sel),
-                  __builtin_amdgcn_perm(reg[3][w], reg[2][w], sel)};
-      *reinterpret_cast<u32x2*>(vt + lds_off + e * T::VSTR) = pk;
-    }
-  }
-};
-
-template <int D, int NW>
-__device__ __forceinline__ void qk_tile(const uint16_t* ks, const f16x8 (&qf)[D / 16], int l32, int h2,
-                                        f32x16 (&s)[2]) {
-  using T = Tile<D, NW>;
+// S^T = K·Q^T for one tile: lane (n, h2) reads chunk 2c + h2 of K row 32kb + n
+// (koff[c] holds that row-in-block and swizzled chunk; kb adds 32 rows).
+template <int D>
+__device__ __forceinline__ void qk_tile(const uint16_t* ks, const int (&koff)[D / 16],
+                                        const f16x8 (&qf)[D / 16], f32x16 (&s)[2]) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -239,22 +275,43 @@ __device__ __forceinline__ void qk_tile(const uint16_t* ks, const f16x8 (&qf)[D 
   for (int c = 0; c < D / 16; ++c) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const f16x8 a = *reinterpret_cast<const f16x8*>(ks + (kb * 32 + l32) * T::KSTR + 16 * c + 8 * h2);
+      const f16x8 a = *reinterpret_cast<const f16x8*>(ks + kb * 32 * D + koff[c]);
       s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[c], s[kb], 0, 0, 0);
     }
   }
 }
 
+// A operand of O^T += V^T·P^T for d-block db and 16-key chunk kc, read from the
+// row-major V tile with two transposing reads.  Lane l (i = l % 16, group
+// G = l / 16, h2 = l / 32) needs V[key][32db + l % 32] for the keys
+// 16kc + 4h2 + {0..3} (elements 0-3) and 16kc + 8 + 4h2 + {0..3} (4-7): the
+// order of the S^T accumulator rows that form the B operand.  In each read,
+// lane i of a 16-lane group fetches 4 d-values (32db + 16(G%2) + 4(i%4) ..)
+// of key (base + i/4) and the hardware hands lane i the i-th of them from the
+// four keys; voff[db] holds this lane's swizzled address for kc = 0.
+template <int D>
+__device__ __forceinline__ bf16x8 pv_operand(const uint16_t* vt, const int (&voff)[D / 32], int db,
+                                             int kc) {
+  const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vt + voff[db] + kc * 16 * D));
+  const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vt + voff[db] + (kc * 16 + 8) * D));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 template <int D, int KMODE, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnParams p) {
   using T = Tile<D, NW>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::K_ELEMS + 2 * T::V_ELEMS];
-  auto ks_buf = [&](int i) { return smem + i * T::K_ELEMS; };
-  auto vs_buf = [&](int i) { return smem + 2 * T::K_ELEMS + i * T::V_ELEMS; };
+  // Stages of (K, V) tiles in LDS, one array each so that the compiler can
+  // tell the in-flight copies into one stage from the reads of another.
+  // Pre-rotated f16 K and V are copied straight to LDS, three stages deep;
+  // K converted on the way goes through registers, two stages.
+  constexpr int NST = KMODE == 0 ? 3 : 2;
+  constexpr int E3 = NST > 2 ? T::ELEMS : 8;
+  __shared__ __attribute__((aligned(1024))) uint16_t k_st0[T::ELEMS], k_st1[T::ELEMS], k_st2[E3];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_st0[T::ELEMS], v_st1[T::ELEMS], v_st2[E3];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int h2 = lane >> 5;
 
@@ -333,10 +390,26 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
   const int64_t wqpos_min = p.q_pos0 + wrow0;
   const int64_t wqpos_max = p.q_pos0 + (wq_last >= wrow0 ? wq_last : wrow0);
 
-  KStager<D, NW, KMODE> kst;
-  VStager<D, NW> vst;
-  kst.init(p, kbase, tid);
-  vst.init(p, vbase, tid);
+  // ---- staging and per-lane LDS read offsets
+  LdsCopy<D, NW, true> kcp;
+  LdsCopy<D, NW, false> vcp;
+  KRegStage<D, NW, KMODE == 0 ? 1 : KMODE> kreg;
+  if constexpr (KMODE == 0)
+    kcp.init(kbase, p.ks_s, p.n_kv, wave, lane);
+  else
+    kreg.init(p, kbase, tid);
+  vcp.init(vbase, p.vs_s, p.n_kv, wave, lane);
+  int koff[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) koff[c] = l32 * D + 8 * ((2 * c + h2) ^ k_swz<D>(l32));
+  int voff[D / 32];
+  {
+    const int i = lane & 15, gg = (lane >> 4) & 1;
+    const int r = 4 * h2 + (i >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+      voff[db] = r * D + 8 * ((4 * db + 2 * gg + ((i & 3) >> 1)) ^ v_swz<D>(r)) + 4 * (i & 1);
+  }
 
   // ---- per-tile pieces of the online softmax
   // mask S(t) (only for tiles that straddle a mask edge for this wave)
@@ -410,38 +483,67 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + (db * 32 + l32) * T::VSTR + 16 * kc + 8 * h2);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kc], oacc[db], 0, 0, 0);
-      }
+      for (int kc = 0; kc < 4; ++kc)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv_operand<D>(vt, voff, db, kc), pf[kc],
+                                                           oacc[db], 0, 0, 0);
     }
   };
 
-  {
-    // ---- one tile at a time: S(t), softmax, PV; tile t+1's global loads in
-    // flight meanwhile, staged into the other buffer at the end
-    if (ntl > 0) {
-      kst.load(tile_j0(0));
-      vst.load(tile_j0(0));
-      kst.store(ks_buf(0));
-      vst.store(vs_buf(0));
+  // ---- the tile loop: step t computes tile t from stage t % NST while the
+  // copy of tile t + NST - 1 is in flight, then waits for its own copies of
+  // tile t + 1 and meets the other waves at the barrier (after which stage
+  // t % NST may be overwritten).  The loop is unrolled NST times so that every
+  // step names its stage arrays directly.
+  constexpr int kLoadsPerTile = KMODE == 0 ? 2 * T::LPW : T::LPW;  // vector memory ops per wave
+  auto issue = [&](uint16_t* ks, uint16_t* vs, int t) {
+    const int j0 = tile_j0(t);
+    if constexpr (KMODE == 0) kcp.issue(ks, j0);
+    vcp.issue(vs, j0);
+  };
+  auto step = [&](const uint16_t* ks, const uint16_t* vs, uint16_t* ks_next, uint16_t* vs_next,
+                  int t) {
+    const int tn = t + NST - 1;
+    const bool pre = tn < ntl;
+    if (pre) {
+      if constexpr (KMODE != 0) kreg.load(tile_j0(tn));
+      issue(ks_next, vs_next, tn);
     }
-    __syncthreads();
-    for (int t = 0; t < ntl; ++t) {
-      if (t + 1 < ntl) {
-        kst.load(tile_j0(t + 1));
-        vst.load(tile_j0(t + 1));
-      }
-      f32x16 s_cur[2];
-      qk_tile<D, NW>(ks_buf(t & 1), qf, l32, h2, s_cur);
-      mask_tile(s_cur, tile_j0(t));
-      rescale(tile_max(s_cur));
-      exp_pv(s_cur, vs_buf(t & 1));
-      if (t + 1 < ntl) {  // the other buffer was last read before the previous barrier
-        kst.store(ks_buf((t + 1) & 1));
-        vst.store(vs_buf((t + 1) & 1));
-      }
-      __syncthreads();
+    f32x16 s_cur[2];
+    qk_tile<D>(ks, koff, qf, s_cur);
+    mask_tile(s_cur, tile_j0(t));
+    rescale(tile_max(s_cur));
+    exp_pv(s_cur, vs);
+    if constexpr (KMODE != 0) {
+      if (pre) kreg.store(ks_next);
+    }
+    if (NST > 2 && pre)
+      stage_barrier<kLoadsPerTile>();
+    else
+      stage_barrier<0>();
+  };
+
+  if (ntl > 0) {
+    if constexpr (KMODE != 0) {
+      kreg.load(tile_j0(0));
+      kreg.store(k_st0);
+    }
+    issue(k_st0, v_st0, 0);
+  }
+  if (NST > 2 && ntl > 1) issue(k_st1, v_st1, 1);
+  // draining here costs one copy latency per workgroup and gives the loop a
+  // single entry state, in which the compiler can tell the stages apart
+  stage_barrier<0>();
+  for (int t = 0; t < ntl; t += NST) {
+    if constexpr (NST > 2) {
+      step(k_st0, v_st0, k_st2, v_st2, t);
+      if (t + 1 >= ntl) break;
+      step(k_st1, v_st1, k_st0, v_st0, t + 1);
+      if (t + 2 >= ntl) break;
+      step(k_st2, v_st2, k_st1, v_st1, t + 2);
+    } else {
+      step(k_st0, v_st0, k_st1, v_st1, t);
+      if (t + 1 >= ntl) break;
+      step(k_st1, v_st1, k_st0, v_st0, t + 1);
     }
   }
 
@@ -506,6 +608,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     if (h2 == 0) *lse_ptr = lse_m;
   }
 }
+
+// Explicit instantiations: with only the implicit ones from launch_dn, the
+// host pass emitted the launch stub of the first k_mode of each head size
+// and left the others undefined (the library then fails to load).
+template __global__ void attn_fwd_kernel<64, 0, kNWd64>(const AttnParams);
+template __global__ void attn_fwd_kernel<64, 1, kNWd64>(const AttnParams);
+template __global__ void attn_fwd_kernel<64, 2, kNWd64>(const AttnParams);
+template __global__ void attn_fwd_kernel<128, 0, kNWd128>(const AttnParams);
+template __global__ void attn_fwd_kernel<128, 1, kNWd128>(const AttnParams);
+template __global__ void attn_fwd_kernel<128, 2, kNWd128>(const AttnParams);
 
 template <int D, int NW>
 hipError_t launch_dn(const AttnParams& p, hipStream_t s, unsigned grid) {
