@@ -114,7 +114,7 @@ lcx_status lcx_rope_apply_qk(const void* q, void* q_out, const void* k, void* k_
 typedef struct {
   const void* q; /* [B][Hq][n_q][d]; bf16 raw (rope_q = 1) or pre-rotated bf16/f16 */
   const void* k; /* [B][Hkv][n_kv][d]; bf16 raw (rope_k = 1) or pre-rotated bf16/f16 */
-  const void* v; /* [B][Hkv][n_kv][d]; bf16, never rotated */
+  const void* v; /* [B][Hkv][n_kv][d]; bf16, never rotated; or the tile layout (v_tiled) */
   int32_t q_dtype, k_dtype; /* LCX_BF16 or LCX_F16 (F16 only when pre-rotated) */
   int32_t B, Hq, Hkv, d;    /* Hq % Hkv == 0; d in {64, 128} */
   int64_t n_q, n_kv;
@@ -134,6 +134,8 @@ typedef struct {
   int32_t o_dtype;          /* LCX_BF16 or LCX_F32 */
   float* lse;               /* fp32 [B][Hq][n_q], natural log; -inf for a row with no key */
   int32_t accumulate;       /* 1: merge into the existing (o f32, lse) in the epilogue */
+  int32_t v_tiled;          /* 1: v is in the tile layout of lcx_attn_pack_v; v_strides[0..1]
+                               are its batch and head strides (elements), v_strides[2] unused */
 } lcx_attn_args;
 
 /*
@@ -150,6 +152,26 @@ typedef struct {
  * UNSUPPORTED for d not 64/128, causal == 0, non-16-byte-aligned rows.
  */
 lcx_status lcx_attn_fwd(const lcx_attn_args* a, hipStream_t stream);
+
+/*
+ * Layout step for the PV product (V is not transformed): V copied into the
+ * tile layout that lcx_attn_fwd reads with v_tiled = 1, so that each MFMA
+ * operand of O += P·V is one 16-byte LDS read (the same role as the
+ * pre-rotation of K by lcx_rope_apply_qk).  [上下文擴充套件 FlashAttention 的分塊計算策略]
+ *   v        [B][Hkv][n][d] bf16, strides v_strides (elements), rows 16-byte aligned
+ *   v_tiles  [B][Hkv][T][d][64] bf16, T = ceil(n / 64), contiguous, caller-owned:
+ *            tile t, row e holds V[64t + key][e] for the 64 keys of the tile,
+ *            the keys of each 16-key group in the order 0-3, 8-11, 4-7, 12-15
+ *            (the row order of the QK^T accumulator); keys >= n are zeros.
+ * For lcx_attn_args: v = v_tiles, v_tiled = 1, v_strides = {Hkv·T·64·d, T·64·d, 0}.
+ * A call over a key range [j0, j0 + n_kv) of the packed buffer passes
+ * v = v_tiles + (j0 / 64)·64·d with j0 a multiple of 64 (the chunked driver
+ * needs chunk % 64 == 0).
+ * Errors: INVALID_ARG for NULL pointers, B/Hkv < 1, n < 1, negative strides;
+ * UNSUPPORTED for d not 64 or 128, unaligned pointers or rows.
+ */
+lcx_status lcx_attn_pack_v(const void* v, void* v_tiles, int32_t B, int32_t Hkv, int64_t n,
+                           int32_t d, const int64_t v_strides[3], hipStream_t stream);
 
 /*
  * Step a9: acc <- merge(acc, part) row by row over [B][H][rows]:

@@ -44,7 +44,7 @@ class AttnArgs(ctypes.Structure):
                 ("cos_tab", _vp), ("sin_tab", _vp), ("tab_pos0", _i64), ("tab_len", _i64),
                 ("rope", ctypes.POINTER(RopeCfg)), ("softmax_scale", _f32), ("causal", _i32),
                 ("window", _i64), ("n_sink", _i32), ("o", _vp), ("o_dtype", _i32),
-                ("lse", _vp), ("accumulate", _i32)]
+                ("lse", _vp), ("accumulate", _i32), ("v_tiled", _i32)]
 
 
 _P3 = ctypes.POINTER(_i64)
@@ -64,6 +64,8 @@ _lib.lcx_attn_merge.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i64, _i32, _P3,
 _lib.lcx_attn_merge.restype = ctypes.c_int
 _lib.lcx_attn_fwd_chunked.argtypes = [ctypes.POINTER(AttnArgs), _i64, _vp, _vp, _vp, _vp, _vp]
 _lib.lcx_attn_fwd_chunked.restype = ctypes.c_int
+_lib.lcx_attn_pack_v.argtypes = [_vp, _vp, _i32, _i32, _i64, _i32, _P3, _vp]
+_lib.lcx_attn_pack_v.restype = ctypes.c_int
 
 
 class LcxError(RuntimeError):
@@ -152,7 +154,12 @@ def _attn_args(q, k, v, o, lse, *, rope_q, rope_k, cos, sin, tab_pos0, cfg, soft
     a.q_dtype, a.k_dtype = _DT[q.dtype], _DT[k.dtype]
     a.B, a.Hq, a.Hkv, a.d = B, Hq, Hkv, d
     a.n_q, a.n_kv = n_q, n_kv
-    a.q_strides, a.k_strides, a.v_strides = _s3(q), _s3(k), _s3(v)
+    a.q_strides, a.k_strides = _s3(q), _s3(k)
+    if v.dim() == 5:  # tile layout from pack_v: [B, Hkv, T, d, 64]
+        a.v_strides = (_i64 * 3)(v.stride(0), v.stride(1), 0)
+        a.v_tiled = 1
+    else:
+        a.v_strides = _s3(v)
     a.o_strides = _s3(o)
     if lse.stride(2) != 1:
         raise ValueError("lse rows must be contiguous")
@@ -173,10 +180,24 @@ def _attn_args(q, k, v, o, lse, *, rope_q, rope_k, cos, sin, tab_pos0, cfg, soft
     return a
 
 
+def pack_v(v, out=None):
+    """lcx_attn_pack_v: v [B,Hkv,n,d] bf16 -> tile layout [B,Hkv,ceil(n/64),d,64] bf16,
+    accepted by attn_fwd / attn_fwd_chunked in place of v."""
+    B, Hkv, n, d = v.shape
+    T = (n + 63) // 64
+    if out is None:
+        out = torch.empty((B, Hkv, T, d, 64), dtype=v.dtype, device=v.device)
+    if tuple(out.shape) != (B, Hkv, T, d, 64) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, Hkv, T, d, 64] tensor")
+    _check(_lib.lcx_attn_pack_v(_ptr(v), _ptr(out), B, Hkv, n, d, _s3(v), _stream(v)))
+    return out
+
+
 def attn_fwd(q, k, v, o=None, lse=None, *, rope_q=False, rope_k=False, cos=None, sin=None,
              tab_pos0=0, rope=None, softmax_scale=0.0, window=-1, n_sink=0, q_pos0=0, k_pos0=0,
              accumulate=False, out_dtype=torch.bfloat16, causal=True):
-    """lcx_attn_fwd.  q [B,Hq,n_q,d], k/v [B,Hkv,n_kv,d].  Returns (o, lse)."""
+    """lcx_attn_fwd.  q [B,Hq,n_q,d], k [B,Hkv,n_kv,d], v [B,Hkv,n_kv,d] or its pack_v
+    tile layout.  Returns (o, lse)."""
     B, Hq, n_q, d = q.shape
     if o is None:
         o = torch.empty((B, Hq, n_q, d), dtype=out_dtype, device=q.device)

@@ -196,6 +196,40 @@ struct LdsCopy {
   }
 };
 
+// Copy of one V tile in the 64-key tile layout (d rows of 64 keys, 128 bytes
+// each; contiguous in HBM) into LDS, row r's chunk c in slot c ^ vt_swz(r):
+// per wave LPW loads, lane L of load i fills row (wave·LPW + i)·8 + L / 8,
+// slot L % 8.  Tiles are whole in HBM (the packer zero-fills past the last
+// key), so the resource covers exactly one tile.
+__device__ __forceinline__ int vt_swz(int r) { return (r >> 1) & 7; }
+
+template <int D, int NW>
+struct LdsCopyVT {
+  static constexpr int LPW = D * 128 / 1024 / NW;
+  static_assert(LPW >= 1 && D * 128 == LPW * NW * 1024, "V tile split");
+  const uint16_t* base;
+  int row0;
+  uint32_t off[LPW];
+
+  __device__ __forceinline__ void init(const uint16_t* b, int wave, int lane) {
+    base = b;
+    row0 = wave * LPW * 8;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int r = row0 + i * 8 + lane / 8;
+      off[i] = (uint32_t)(r * 128) + (uint32_t)(((lane % 8) ^ vt_swz(r)) * 16);
+    }
+  }
+  __device__ __forceinline__ void issue(uint16_t* lds, int j0) const {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (int64_t)(j0 / BN) * (D * BN), D * BN * 2);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const uint32_t la = (uint32_t)(uintptr_t)(lds_void*)(lds + (row0 + i * 8) * BN);
+      lds_copy16(r, off[i], __builtin_amdgcn_readfirstlane(la));
+    }
+  }
+};
+
 // K staging through registers for K that is converted on the way (bf16 -> f16,
 // or rotated from the fp32 tables): global (buffer loads) -> registers -> LDS
 // in the swizzled layout above.
@@ -281,23 +315,30 @@ __device__ __forceinline__ void qk_tile(const uint16_t* ks, const int (&koff)[D 
   }
 }
 
-// A operand of O^T += V^T·P^T for d-block db and 16-key chunk kc, read from the
-// row-major V tile with two transposing reads.  Lane l (i = l % 16, group
-// G = l / 16, h2 = l / 32) needs V[key][32db + l % 32] for the keys
-// 16kc + 4h2 + {0..3} (elements 0-3) and 16kc + 8 + 4h2 + {0..3} (4-7): the
-// order of the S^T accumulator rows that form the B operand.  In each read,
-// lane i of a 16-lane group fetches 4 d-values (32db + 16(G%2) + 4(i%4) ..)
-// of key (base + i/4) and the hardware hands lane i the i-th of them from the
-// four keys; voff[db] holds this lane's swizzled address for kc = 0.
-template <int D>
-__device__ __forceinline__ bf16x8 pv_operand(const uint16_t* vt, const int (&voff)[D / 32], int db,
-                                             int kc) {
-  const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vt + voff[db] + kc * 16 * D));
-  const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vt + voff[db] + (kc * 16 + 8) * D));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+// A operand of O^T += V^T·P^T for d-block db and 16-key chunk kc.  Lane l
+// (i = l % 16, group G = l / 16, h2 = l / 32) needs V[key][32db + l % 32] for
+// the keys 16kc + 4h2 + {0..3} (elements 0-3) and 16kc + 8 + 4h2 + {0..3}
+// (4-7): the order of the S^T accumulator rows that form the B operand.
+// From the 64-key tile layout (VT) that is one 16-byte read.  From a
+// row-major V tile it takes two transposing reads: lane i of a 16-lane group
+// fetches 4 d-values (32db + 16(G%2) + 4(i%4) ..) of key (base + i/4) and
+// the hardware hands lane i the i-th of them from the four keys; voff[db]
+// holds this lane's swizzled address for kc = 0.
+template <int D, bool VT>
+__device__ __forceinline__ bf16x8 pv_operand(const uint16_t* vt, const int (&voff)[4], int db, int kc) {
+  if constexpr (VT) {
+    // tile layout: row 32db + l32 holds the keys already in accumulator order,
+    // so the 8 values are chunk 2kc + h2 of that row; voff[kc] is this lane's
+    // swizzled address for db = 0
+    return *reinterpret_cast<const bf16x8*>(vt + voff[kc] + db * 32 * BN);
+  } else {
+    const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vt + voff[db] + kc * 16 * D));
+    const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vt + voff[db] + (kc * 16 + 8) * D));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
 }
 
-template <int D, int KMODE, int NW>
+template <int D, int KMODE, int NW, bool VT>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnParams p) {
   using T = Tile<D, NW>;
   // Stages of (K, V) tiles in LDS, one array each so that the compiler can
@@ -393,17 +434,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
   // ---- staging and per-lane LDS read offsets
   LdsCopy<D, NW, true> kcp;
   LdsCopy<D, NW, false> vcp;
+  LdsCopyVT<D, NW> vtcp;
   KRegStage<D, NW, KMODE == 0 ? 1 : KMODE> kreg;
   if constexpr (KMODE == 0)
     kcp.init(kbase, p.ks_s, p.n_kv, wave, lane);
   else
     kreg.init(p, kbase, tid);
-  vcp.init(vbase, p.vs_s, p.n_kv, wave, lane);
+  if constexpr (VT)
+    vtcp.init(vbase, wave, lane);
+  else
+    vcp.init(vbase, p.vs_s, p.n_kv, wave, lane);
   int koff[D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) koff[c] = l32 * D + 8 * ((2 * c + h2) ^ k_swz<D>(l32));
-  int voff[D / 32];
-  {
+  int voff[4] = {0, 0, 0, 0};
+  if constexpr (VT) {
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) voff[kc] = l32 * BN + 8 * ((2 * kc + h2) ^ vt_swz(l32));
+  } else {
     const int i = lane & 15, gg = (lane >> 4) & 1;
     const int r = 4 * h2 + (i >> 2);
 #pragma unroll
@@ -484,7 +532,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc)
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv_operand<D>(vt, voff, db, kc), pf[kc],
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv_operand<D, VT>(vt, voff, db, kc), pf[kc],
                                                            oacc[db], 0, 0, 0);
     }
   };
@@ -498,7 +546,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
   auto issue = [&](uint16_t* ks, uint16_t* vs, int t) {
     const int j0 = tile_j0(t);
     if constexpr (KMODE == 0) kcp.issue(ks, j0);
-    vcp.issue(vs, j0);
+    if constexpr (VT)
+      vtcp.issue(vs, j0);
+    else
+      vcp.issue(vs, j0);
   };
   auto step = [&](const uint16_t* ks, const uint16_t* vs, uint16_t* ks_next, uint16_t* vs_next,
                   int t) {
@@ -612,22 +663,31 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
 // Explicit instantiations: with only the implicit ones from launch_dn, the
 // host pass emitted the launch stub of the first k_mode of each head size
 // and left the others undefined (the library then fails to load).
-template __global__ void attn_fwd_kernel<64, 0, kNWd64>(const AttnParams);
-template __global__ void attn_fwd_kernel<64, 1, kNWd64>(const AttnParams);
-template __global__ void attn_fwd_kernel<64, 2, kNWd64>(const AttnParams);
-template __global__ void attn_fwd_kernel<128, 0, kNWd128>(const AttnParams);
-template __global__ void attn_fwd_kernel<128, 1, kNWd128>(const AttnParams);
-template __global__ void attn_fwd_kernel<128, 2, kNWd128>(const AttnParams);
+#define LCX_ATTN_INST(D, NW)                                                       \
+  template __global__ void attn_fwd_kernel<D, 0, NW, false>(const AttnParams);    \
+  template __global__ void attn_fwd_kernel<D, 1, NW, false>(const AttnParams);    \
+  template __global__ void attn_fwd_kernel<D, 2, NW, false>(const AttnParams);    \
+  template __global__ void attn_fwd_kernel<D, 0, NW, true>(const AttnParams);     \
+  template __global__ void attn_fwd_kernel<D, 1, NW, true>(const AttnParams);     \
+  template __global__ void attn_fwd_kernel<D, 2, NW, true>(const AttnParams);
+LCX_ATTN_INST(64, kNWd64)
+LCX_ATTN_INST(128, kNWd128)
+#undef LCX_ATTN_INST
+
+template <int D, int NW, bool VT>
+hipError_t launch_dv(const AttnParams& p, hipStream_t s, unsigned grid) {
+  const dim3 block(64 * NW);
+  switch (p.k_mode) {
+    case 0: hipLaunchKernelGGL((attn_fwd_kernel<D, 0, NW, VT>), dim3(grid), block, 0, s, p); break;
+    case 1: hipLaunchKernelGGL((attn_fwd_kernel<D, 1, NW, VT>), dim3(grid), block, 0, s, p); break;
+    default: hipLaunchKernelGGL((attn_fwd_kernel<D, 2, NW, VT>), dim3(grid), block, 0, s, p); break;
+  }
+  return hipGetLastError();
+}
 
 template <int D, int NW>
 hipError_t launch_dn(const AttnParams& p, hipStream_t s, unsigned grid) {
-  const dim3 block(64 * NW);
-  switch (p.k_mode) {
-    case 0: hipLaunchKernelGGL((attn_fwd_kernel<D, 0, NW>), dim3(grid), block, 0, s, p); break;
-    case 1: hipLaunchKernelGGL((attn_fwd_kernel<D, 1, NW>), dim3(grid), block, 0, s, p); break;
-    default: hipLaunchKernelGGL((attn_fwd_kernel<D, 2, NW>), dim3(grid), block, 0, s, p); break;
-  }
-  return hipGetLastError();
+  return p.v_tiled ? launch_dv<D, NW, true>(p, s, grid) : launch_dv<D, NW, false>(p, s, grid);
 }
 
 }  // namespace

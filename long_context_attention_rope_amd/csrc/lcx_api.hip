@@ -148,7 +148,10 @@ lcx_status check_attn(const lcx_attn_args* a, bool chunked) {
   }
   if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
     return fail(LCX_ERR_UNSUPPORTED, "q, k, v, o must be 16-byte aligned");
-  if (!strides_ok(a->q_strides, 8) || !strides_ok(a->k_strides, 8) || !strides_ok(a->v_strides, 8))
+  if (a->v_tiled != 0 && a->v_tiled != 1) return fail(LCX_ERR_INVALID_ARG, "v_tiled must be 0 or 1");
+  // tile layout: only the batch and head strides are used
+  const int64_t v_st[3] = {a->v_strides[0], a->v_strides[1], a->v_tiled ? 8 : a->v_strides[2]};
+  if (!strides_ok(a->q_strides, 8) || !strides_ok(a->k_strides, 8) || !strides_ok(v_st, 8))
     return fail(LCX_ERR_UNSUPPORTED, "q/k/v strides must be non-negative multiples of 8 elements");
   if (!strides_ok(a->o_strides, a->o_dtype == LCX_F32 ? 4 : 8))
     return fail(LCX_ERR_UNSUPPORTED, "o strides must keep rows 16-byte aligned");
@@ -156,7 +159,7 @@ lcx_status check_attn(const lcx_attn_args* a, bool chunked) {
     return fail(LCX_ERR_INVALID_ARG, "lse strides must be >= 0");
   // the kernel addresses one KV head's keys with 32-bit buffer offsets
   const int64_t lim = (int64_t)1 << 31;
-  if (a->n_kv * a->k_strides[2] * 2 >= lim || a->n_kv * a->v_strides[2] * 2 >= lim ||
+  if (a->n_kv * a->k_strides[2] * 2 >= lim || (!a->v_tiled && a->n_kv * a->v_strides[2] * 2 >= lim) ||
       (a->rope_k && a->n_kv * a->d * 2 >= lim))
     return fail(LCX_ERR_UNSUPPORTED, "one KV head spans 2 GiB or more (split the keys into chunks)");
   const int bm = lcx::attn_rows_per_block(a->d);
@@ -196,6 +199,7 @@ lcx::AttnParams make_params(const lcx_attn_args* a) {
   p.k_mode = a->rope_k ? 2 : (a->k_dtype == LCX_BF16 ? 1 : 0);
   p.o_mode = a->o_dtype == LCX_BF16 ? 0 : (a->accumulate ? 2 : 1);
   p.causal = a->causal;
+  p.v_tiled = a->v_tiled;
   return p;
 }
 
@@ -310,6 +314,25 @@ lcx_status lcx_attn_fwd(const lcx_attn_args* a, hipStream_t stream) {
   return hip_status(lcx::launch_attn_fwd(make_params(a), stream), "attention launch");
 }
 
+lcx_status lcx_attn_pack_v(const void* v, void* v_tiles, int32_t B, int32_t Hkv, int64_t n,
+                           int32_t d, const int64_t v_strides[3], hipStream_t stream) {
+  if (!v || !v_tiles || !v_strides) return fail(LCX_ERR_INVALID_ARG, "v, v_tiles and v_strides are required");
+  if (B < 1 || Hkv < 1 || n < 1) return fail(LCX_ERR_INVALID_ARG, "B, Hkv and n must be >= 1");
+  if (B > 65535 || Hkv > 65535) return fail(LCX_ERR_UNSUPPORTED, "B and Hkv must be <= 65535");
+  if (d != 64 && d != 128) return fail(LCX_ERR_UNSUPPORTED, "head dim %d (kernels: 64, 128)", d);
+  if (v_strides[0] < 0 || v_strides[1] < 0 || v_strides[2] < 0)
+    return fail(LCX_ERR_INVALID_ARG, "strides must be >= 0");
+  if (!strides_ok(v_strides, 8) || !aligned16(v) || !aligned16(v_tiles))
+    return fail(LCX_ERR_UNSUPPORTED, "rows must be 16-byte aligned");
+  lcx::PackVParams p{};
+  p.v = static_cast<const uint16_t*>(v);
+  p.vt = static_cast<uint16_t*>(v_tiles);
+  p.vs_b = v_strides[0]; p.vs_h = v_strides[1]; p.vs_s = v_strides[2];
+  p.B = B; p.Hkv = Hkv; p.d = d; p.n = n;
+  p.n_tiles = (n + 63) / 64;
+  return hip_status(lcx::launch_pack_v(p, stream), "pack launch");
+}
+
 lcx_status lcx_attn_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
                           int32_t B, int32_t H, int64_t rows, int32_t d,
                           const int64_t acc_strides[3], const int64_t part_strides[3],
@@ -349,6 +372,8 @@ lcx_status lcx_attn_fwd_chunked(const lcx_attn_args* a, int64_t chunk, float* o_
   lcx_status st = check_attn(a, true);
   if (st != LCX_OK) return st;
   if (chunk <= 0) return fail(LCX_ERR_INVALID_ARG, "chunk %lld must be > 0", (long long)chunk);
+  if (a->v_tiled && chunk % 64)
+    return fail(LCX_ERR_INVALID_ARG, "chunk %lld must be a multiple of 64 with tiled V", (long long)chunk);
   if (!o_acc || !lse_acc) return fail(LCX_ERR_INVALID_ARG, "o_acc and lse_acc are required");
   if ((o_part == nullptr) != (lse_part == nullptr))
     return fail(LCX_ERR_INVALID_ARG, "o_part and lse_part go together");
@@ -374,7 +399,7 @@ lcx_status lcx_attn_fwd_chunked(const lcx_attn_args* a, int64_t chunk, float* o_
     s.n_q = nq - r0;
     s.q_pos0 = a->q_pos0 + r0;
     s.k = static_cast<const uint16_t*>(a->k) + j0 * a->k_strides[2];
-    s.v = static_cast<const uint16_t*>(a->v) + j0 * a->v_strides[2];
+    s.v = static_cast<const uint16_t*>(a->v) + (a->v_tiled ? (j0 / 64) * 64 * d : j0 * a->v_strides[2]);
     s.n_kv = len;
     s.k_pos0 = a->k_pos0 + j0;
     s.o_dtype = LCX_F32;

@@ -56,6 +56,15 @@ struct AttnParams {
   int32_t o_mode;  // 0: bf16, 1: f32, 2: f32 merged into the existing (o, lse)
   int32_t xcd_map; // 1: XCD-aware block order
   int32_t causal;
+  int32_t v_tiled;  // 1: v in the 64-key tile layout (vs_b, vs_h its strides)
+};
+
+struct PackVParams {
+  const uint16_t* v;
+  uint16_t* vt;
+  int64_t vs_b, vs_h, vs_s;
+  int32_t B, Hkv, d;
+  int64_t n, n_tiles;
 };
 
 struct MergeParams {
@@ -77,6 +86,7 @@ hipError_t launch_rope_table(const RopeTableParams& p, hipStream_t s);
 hipError_t launch_rope_apply(const RopeApplyParams* slots, int n_slots, hipStream_t s);
 hipError_t launch_attn_fwd(const AttnParams& p, hipStream_t s);
 hipError_t launch_attn_merge(const MergeParams& p, hipStream_t s);
+hipError_t launch_pack_v(const PackVParams& p, hipStream_t s);
 // fill (o, lse) rows with the empty state (0, -inf); o fp32 contiguous per row
 hipError_t launch_fill_empty(float* o, float* lse, int32_t B, int32_t H, int64_t rows, int32_t d,
                              int64_t os_b, int64_t os_h, int64_t os_s, int64_t ls_b, int64_t ls_h,

@@ -29,8 +29,8 @@ def _declared():
 
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["lcx_rope_freqs", "lcx_rope_apply_qk", "lcx_attn_fwd",
-                                  "lcx_attn_merge", "lcx_attn_fwd_chunked", "lcx_status_string",
-                                  "lcx_last_error"])
+                                  "lcx_attn_pack_v", "lcx_attn_merge", "lcx_attn_fwd_chunked",
+                                  "lcx_status_string", "lcx_last_error"])
 
 
 def test_library_exports_every_declared_symbol(lcx):
@@ -136,6 +136,7 @@ ATTN_BAD = [
     (1, dict(rope_q=1, cos_tab=FAKE, sin_tab=FAKE, tab_len=256, q_pos0=1)),
     (1, dict(accumulate=1)), (1, dict(o_dtype=7)), (1, dict(softmax_scale=-1.0)),
     (2, dict(q=FAKE + 2)), (2, dict(q_strides=(ctypes.c_int64 * 3)(0, 0, 60))),
+    (1, dict(v_tiled=2)), (2, dict(v_tiled=1, v_strides=(ctypes.c_int64 * 3)(12, 16384, 0))),
 ]
 
 
@@ -152,6 +153,20 @@ def test_chunked_rejects(lcx):
     assert lcx._lib.lcx_attn_fwd_chunked(ctypes.byref(a), 64, FAKE, FAKE, FAKE, None, None) == 1
     a2 = _args(lcx, o_dtype=lcx.F32, accumulate=1)
     assert lcx._lib.lcx_attn_fwd_chunked(ctypes.byref(a2), 64, FAKE, FAKE, None, None, None) == 1
+    # tiled V: chunks must start on a 64-key tile
+    a3 = _args(lcx, o_dtype=lcx.F32, v_tiled=1, v_strides=(ctypes.c_int64 * 3)(16384, 16384, 0))
+    assert lcx._lib.lcx_attn_fwd_chunked(ctypes.byref(a3), 96, FAKE, FAKE, None, None, None) == 1
+
+
+def test_pack_v_rejects(lcx):
+    st = (ctypes.c_int64 * 3)(256 * 64, 256 * 64, 64)
+    f = lcx._lib.lcx_attn_pack_v
+    assert f(None, FAKE, 1, 1, 256, 64, st, None) == 1
+    assert f(FAKE, FAKE, 1, 1, 0, 64, st, None) == 1
+    assert f(FAKE, FAKE, 0, 1, 256, 64, st, None) == 1
+    assert f(FAKE, FAKE, 1, 1, 256, 96, st, None) == 2
+    assert f(FAKE + 8, FAKE, 1, 1, 256, 64, st, None) == 2
+    assert f(FAKE, FAKE, 1, 1, 256, 64, (ctypes.c_int64 * 3)(256 * 64, 256 * 64, 60), None) == 2
 
 
 def test_rope_apply_rejects(lcx):

@@ -26,8 +26,10 @@ def _cfg(lcx, w):
 
 
 def _run(lcx, w, q, k, v, *, k_mode="pre_f16", out_dtype=torch.bfloat16, q_pos0=0, k_pos0=0,
-         tab_n=None):
+         tab_n=None, v_tiled=False):
     qd, kd, vd = U.to_dev(q), U.to_dev(k), U.to_dev(v)
+    if v_tiled:
+        vd = lcx.pack_v(vd)
     cfg = _cfg(lcx, w)
     n_tab = tab_n or max(q_pos0 + q.shape[2], k_pos0 + k.shape[2])
     cos, sin = lcx.rope_tables(cfg, n_tab, device=U.dev())
@@ -52,14 +54,42 @@ def _all(w, q, k, v, q_pos0=0, k_pos0=0):
     return o_ref, l_ref
 
 
+@pytest.mark.parametrize("v_tiled", [False, True], ids=["v_rows", "v_tiles"])
 @pytest.mark.parametrize("k_mode", ["pre_f16", "fused"])
-def test_tiny_workload_full(lcx, k_mode):
+def test_tiny_workload_full(lcx, k_mode, v_tiled):
     w = W.TINY
     q, k, v = U.inputs(w)
-    o, lse = _run(lcx, w, q, k, v, k_mode=k_mode)
+    o, lse = _run(lcx, w, q, k, v, k_mode=k_mode, v_tiled=v_tiled)
     o_ref, l_ref = _all(w, q, k, v)
     U.check(o.float().cpu().numpy().reshape(-1, w.d), lse.cpu().numpy().reshape(-1), o_ref, l_ref,
-            f"tiny/{k_mode}")
+            f"tiny/{k_mode}/{'tiles' if v_tiled else 'rows'}")
+
+
+def _tile_key(p):
+    # position p of a packed tile row holds key _tile_key(p): in each group of
+    # 16 keys the order 0-3, 8-11, 4-7, 12-15 (the QK^T accumulator row order)
+    g, r = divmod(p, 16)
+    return 16 * g + [0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12, 13, 14, 15][r]
+
+
+@pytest.mark.parametrize("n,d,strided", [(1, 64, False), (200, 128, False), (129, 64, True)])
+def test_pack_v_layout_bit_exact(lcx, n, d, strided):
+    B, Hkv = 2, 3
+    v = torch.randn((B, Hkv, n + (5 if strided else 0), d), device=U.dev()).to(torch.bfloat16)
+    if strided:
+        v = v[:, :, 3:3 + n]
+    t = lcx.pack_v(v)
+    torch.cuda.synchronize()
+    T = (n + 63) // 64
+    got = t.view(torch.int16).cpu().numpy()
+    src = v.contiguous().view(torch.int16).cpu().numpy()
+    keys = np.array([_tile_key(p) for p in range(64)])
+    ref = np.zeros((B, Hkv, T, d, 64), np.int16)
+    for tt in range(T):
+        kk = 64 * tt + keys
+        ok = kk < n
+        ref[:, :, tt][..., ok] = np.swapaxes(src[:, :, kk[ok], :], 2, 3)
+    assert got.shape == ref.shape and np.array_equal(got, ref)
 
 
 SMALL = [
@@ -83,10 +113,10 @@ def test_small_shapes_full(lcx, name, Hq, Hkv, d, n, scheme, window, n_sink, B):
                    cur_len=256, window=window, n_sink=n_sink, seed=100 + n)
     q, k, v = U.inputs(w)
     o_ref, l_ref = _all(w, q, k, v)
-    for k_mode in ("pre_f16", "fused"):
-        o, lse = _run(lcx, w, q, k, v, k_mode=k_mode)
+    for k_mode, v_tiled in (("pre_f16", False), ("pre_f16", True), ("fused", False), ("fused", True)):
+        o, lse = _run(lcx, w, q, k, v, k_mode=k_mode, v_tiled=v_tiled)
         U.check(o.float().cpu().numpy().reshape(-1, d), lse.cpu().numpy().reshape(-1), o_ref, l_ref,
-                f"{name}/{k_mode}")
+                f"{name}/{k_mode}/{'tiles' if v_tiled else 'rows'}")
 
 
 def test_f32_output_and_bf16_prerotated_k(lcx):
@@ -107,13 +137,14 @@ def test_query_and_key_offsets_and_empty_rows(lcx):
     w = W.TINY.with_(seed=8)
     q, _, _ = U.inputs(w, n_q=200)
     _, k, v = U.inputs(w, n_kv=350)
-    o, lse = _run(lcx, w, q, k, v, q_pos0=500, k_pos0=300, tab_n=700)
     bb = np.zeros(w.Hq * 200, np.int32)
     hh = np.repeat(np.arange(w.Hq), 200).astype(np.int32)
     rr = np.tile(np.arange(200), w.Hq)
     o_ref, l_ref = U.oracle_rows(w, q, k, v, bb, hh, rr, q_pos0=500, k_pos0=300)
-    U.check(o.float().cpu().numpy().reshape(-1, w.d), lse.cpu().numpy().reshape(-1), o_ref, l_ref,
-            "offsets")
+    for v_tiled in (False, True):
+        o, lse = _run(lcx, w, q, k, v, q_pos0=500, k_pos0=300, tab_n=700, v_tiled=v_tiled)
+        U.check(o.float().cpu().numpy().reshape(-1, w.d), lse.cpu().numpy().reshape(-1), o_ref, l_ref,
+                f"offsets/{'tiles' if v_tiled else 'rows'}")
     o, lse = _run(lcx, w, q, k, v, q_pos0=0, k_pos0=300, tab_n=700)
     l = lse.cpu().numpy().reshape(-1)
     o_np = o.float().cpu().numpy()
@@ -262,6 +293,13 @@ def test_chunked_driver_equals_oracle_and_one_shot(lcx, separate):
     d_o = (acc_o - o1).abs()
     assert d_o.max().item() < U.O_MAX_ABS and d_o.mean().item() < 1e-4
     assert (acc_l - l1).abs().max().item() < 5e-5
+    # the same chunks over tiled V: bit-identical values feed the same MFMAs
+    vt = lcx.pack_v(vd)
+    acc_o2, acc_l2 = torch.empty_like(acc_o), torch.empty_like(acc_l)
+    o2, lse2 = lcx.attn_fwd_chunked(qd, kr, vt, w.chunk, acc_o2, acc_l2, o_part=part_o,
+                                    lse_part=part_l, rope_q=True, cos=cos, sin=sin, rope=cfg)
+    torch.cuda.synchronize()
+    assert torch.equal(acc_o2, acc_o) and torch.equal(acc_l2, acc_l)
 
 
 def test_accumulate_two_halves_equals_one_shot(lcx):
