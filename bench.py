@@ -4,6 +4,7 @@ One step = the whole hot path over one batch of synthetic input that is
 already resident in HBM:
   1. lcx_rope_freqs     frequencies (host, fp64) + cos/sin tables (GPU)
   2. lcx_rope_apply_qk  K rotated once into f16
+     lcx_attn_pack_v    V copied into 64-key tiles (PV operand layout)
   3. lcx_attn_fwd       causal GQA attention, RoPE fused into the Q load,
                         O (bf16) + LSE (fp32)
 on the Llama-3-70B-shaped layer: B=1, 64 query / 8 KV heads, d=128,
@@ -94,6 +95,8 @@ def main():
     ap.add_argument("--workload", default="llama3_70b_128k_dynntk")
     ap.add_argument("--k-mode", choices=["prerotate", "fused"], default="prerotate",
                     help="K rotated once by lcx_rope_apply_qk (default) or inside the attention tile load")
+    ap.add_argument("--v-layout", choices=["tiles", "rows"], default="tiles",
+                    help="V packed into 64-key tiles by lcx_attn_pack_v inside the step (default) or read as rows")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="oracle rows for the CPU baseline (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-merge-check", dest="merge_check", action="store_false",
@@ -132,6 +135,8 @@ def main():
     cos = torch.empty((w.n, half), dtype=torch.float32, device=dev)
     sin = torch.empty((w.n, half), dtype=torch.float32, device=dev)
     k_rot = torch.empty(k.shape, dtype=torch.float16, device=dev)
+    v_tiles = torch.empty((w.B, w.Hkv, (w.n + 63) // 64, w.d, 64), dtype=torch.bfloat16, device=dev)
+    tiled = args.v_layout == "tiles"
     o = torch.empty((w.B, w.Hq, w.n, w.d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.B, w.Hq, w.n), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -142,19 +147,18 @@ def main():
         if ev: ev[1].record(stream)
         if args.k_mode == "prerotate":
             lcx.rope_apply_qk(None, k, cos, sin, k_out=k_rot)
-            if ev: ev[2].record(stream)
-            lcx.attn_fwd(q, k_rot, v, o, lse, rope_q=True, cos=cos, sin=sin, rope=cfg,
-                         window=w.window, n_sink=w.n_sink)
-        else:
-            if ev: ev[2].record(stream)
-            lcx.attn_fwd(q, k, v, o, lse, rope_q=True, rope_k=True, cos=cos, sin=sin, rope=cfg,
-                         window=w.window, n_sink=w.n_sink)
+        if ev: ev[2].record(stream)
+        vv = lcx.pack_v(v, out=v_tiles) if tiled else v
         if ev: ev[3].record(stream)
+        lcx.attn_fwd(q, k_rot if args.k_mode == "prerotate" else k, vv, o, lse, rope_q=True,
+                     rope_k=args.k_mode != "prerotate", cos=cos, sin=sin, rope=cfg,
+                     window=w.window, n_sink=w.n_sink)
+        if ev: ev[4].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -185,7 +189,8 @@ def main():
 
     tab_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     rot_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    pack_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    attn_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in evs]))
     ms_step = wall * 1e3 / args.steps
     flop = w.flop()
     tokens = w.B * w.n
@@ -195,6 +200,7 @@ def main():
 
     tab_bytes = w.n * half * 8
     rot_bytes = w.B * w.Hkv * w.n * w.d * 4 + tab_bytes
+    pack_bytes = w.B * w.Hkv * w.d * 2 * (w.n + 64 * ((w.n + 63) // 64))
 
     out = {
         "metric": METRIC,
@@ -212,15 +218,16 @@ def main():
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "head_dim": w.d, "seq_len": w.n, "rope": w.scheme, "rope_base": w.base,
                    "L_train": w.L_train, "cur_len": w.cur_len, "causal": True,
-                   "k_rope": args.k_mode,
+                   "k_rope": args.k_mode, "v_layout": args.v_layout,
                    "mfma": "QK^T f16 operands, PV bf16 operands, fp32 accumulate"},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
         "kernels_ms": {"rope_table": round(tab_ms, 4), "rope_apply_k": round(rot_ms, 4),
-                       "attn_fwd": round(attn_ms, 3)},
+                       "pack_v": round(pack_ms, 4), "attn_fwd": round(attn_ms, 3)},
         "hbm_gbs": {"rope_table": round(tab_bytes / (tab_ms * 1e-3) / 1e9, 1),
                     "rope_apply_k": round(rot_bytes / (rot_ms * 1e-3) / 1e9, 1)
                     if args.k_mode == "prerotate" else None,
+                    "pack_v": round(pack_bytes / (pack_ms * 1e-3) / 1e9, 1) if tiled else None,
                     "attn_merge": merge_gbs, "peak": PEAK_HBM_GBS},
         "roofline": {"kernel": "attn_fwd", "bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

@@ -1,7 +1,8 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
-benchmark times (tables -> K rotated to f16 -> attention with RoPE fused into
-the Q load), checked on 4096 seeded rows (edge rows on every head plus
-uniform ones) that the fp64 oracle computes one by one."""
+benchmark times (tables -> K rotated to f16, V packed into 64-key tiles ->
+attention with RoPE fused into the Q load), checked on 4096 seeded rows (edge
+rows on every head plus uniform ones) that the fp64 oracle computes one by
+one."""
 import time
 
 import numpy as np
@@ -24,7 +25,8 @@ def _pipeline(lcx, w, qd, kd, vd):
     cfg = lcx.rope_cfg(w.scheme, w.base, w.d, w.L_train, w.L_target, w.cur_len, w.alpha, w.beta)
     cos, sin = lcx.rope_tables(cfg, w.n, device=U.dev())
     _, kr = lcx.rope_apply_qk(None, kd, cos, sin)
-    o, lse = lcx.attn_fwd(qd, kr, vd, rope_q=True, cos=cos, sin=sin, rope=cfg, window=w.window,
+    vt = lcx.pack_v(vd)
+    o, lse = lcx.attn_fwd(qd, kr, vt, rope_q=True, cos=cos, sin=sin, rope=cfg, window=w.window,
                           n_sink=w.n_sink)
     return o, lse, (cfg, cos, sin, kr)
 
@@ -63,11 +65,12 @@ def test_million_token_chunked_sampled(lcx):
     cfg = lcx.rope_cfg(w.scheme, w.base, w.d, w.L_train, w.L_target, w.cur_len, w.alpha, w.beta)
     cos, sin = lcx.rope_tables(cfg, w.n, device=U.dev())
     _, kr = lcx.rope_apply_qk(None, kd, cos, sin)
-    del kd
+    vt = lcx.pack_v(vd)
+    del kd, vd
     acc_o = torch.empty((1, w.Hq, w.n, w.d), dtype=torch.float32, device=U.dev())
     acc_l = torch.empty((1, w.Hq, w.n), dtype=torch.float32, device=U.dev())
     t1 = time.time()
-    o, lse = lcx.attn_fwd_chunked(qd, kr, vd, w.chunk, acc_o, acc_l, rope_q=True, cos=cos, sin=sin,
+    o, lse = lcx.attn_fwd_chunked(qd, kr, vt, w.chunk, acc_o, acc_l, rope_q=True, cos=cos, sin=sin,
                                   rope=cfg)
     torch.cuda.synchronize()
     U.log(f"{w.name}: 128 chunks + merges in {time.time() - t1:.1f}s")
