@@ -338,25 +338,20 @@ __device__ __forceinline__ bf16x8 pv_operand(const uint16_t* vt, const int (&vof
   }
 }
 
-template <int D, int KMODE, int NW, bool VT>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnParams p) {
-  using T = Tile<D, NW>;
-  // Stages of (K, V) tiles in LDS, one array each so that the compiler can
-  // tell the in-flight copies into one stage from the reads of another.
-  // Pre-rotated f16 K and V are copied straight to LDS, three stages deep;
-  // K converted on the way goes through registers, two stages.
-  constexpr int NST = KMODE == 0 ? 3 : 2;
-  constexpr int E3 = NST > 2 ? T::ELEMS : 8;
-  __shared__ __attribute__((aligned(1024))) uint16_t k_st0[T::ELEMS], k_st1[T::ELEMS], k_st2[E3];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_st0[T::ELEMS], v_st1[T::ELEMS], v_st2[E3];
+// Block -> (batch, query head, 256-row query block) and the KV tiles it
+// visits: optional sink tiles, then the window / causal range.  Blocks run
+// longest causal rows first; with xcd_map the G query heads of one KV head
+// are consecutive on one XCD (block id mod 8), sharing its K/V in that L2.
+struct BlockTiles {
+  int b, hq, hkv;
+  int64_t row0;
+  int ntl, sink_n, win_0;
+  __device__ __forceinline__ int j0(int t) const { return (t < sink_n ? t : win_0 + (t - sink_n)) * BN; }
+};
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31;
-  const int h2 = lane >> 5;
-
-  // ---- block -> (b, q head, q block); longest rows first, KV group per XCD
+template <int BM>
+__device__ __forceinline__ BlockTiles block_tiles(const AttnParams& p) {
+  BlockTiles bt;
   const int bid = blockIdx.x;
   int unit, g;
   if (p.xcd_map) {
@@ -368,30 +363,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     unit = bid / p.G;
     g = bid % p.G;
   }
-  const int hkv = unit % p.Hkv;
+  bt.hkv = unit % p.Hkv;
   const int t1 = unit / p.Hkv;
-  const int b = t1 % p.B;
+  bt.b = t1 % p.B;
   const int qrank = t1 / p.B;
   const int qblk = p.n_qblk - 1 - qrank;
-  const int hq = hkv * p.G + g;
+  bt.hq = bt.hkv * p.G + g;
+  bt.row0 = (int64_t)qblk * BM;
 
-  const uint16_t* qbase = p.q + b * p.qs_b + hq * p.qs_h;
-  const uint16_t* kbase = p.k + b * p.ks_b + hkv * p.ks_h;
-  const uint16_t* vbase = p.v + b * p.vs_b + hkv * p.vs_h;
-
-  const int64_t row0 = (int64_t)qblk * T::BM;
-  const int64_t wrow0 = row0 + wave * 32;
-  const int64_t qi = wrow0 + l32;  // this lane's query row
-  const int64_t qpos = p.q_pos0 + qi;
-
-  // ---- Q fragment (RoPE fused here when q_mode == 2)
-  f16x8 qf[D / 16];
-  load_q<D>(p, qbase, qi, h2, qf);
-
-  // ---- KV tile range for the whole block: optional sink tiles, then the
-  // window / causal range
-  const int64_t blk_last = (row0 + T::BM < p.n_q ? row0 + T::BM : p.n_q) - 1;
-  const int64_t qpos_min = p.q_pos0 + row0;
+  const int64_t blk_last = (bt.row0 + BM < p.n_q ? bt.row0 + BM : p.n_q) - 1;
+  const int64_t qpos_min = p.q_pos0 + bt.row0;
   const int64_t qpos_max = p.q_pos0 + blk_last;
   int64_t j_hi = p.n_kv;
   if (p.causal) {
@@ -413,59 +394,42 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     if (sink_t1 > win_t0) sink_t1 = win_t0;
   }
   if (win_t1 < win_t0) win_t1 = win_t0;
-  const int sink_n = (int)sink_t1;
-  const int win_0 = (int)win_t0;
-  const int ntl = (int)(sink_t1 + (win_t1 - win_t0));
-  auto tile_j0 = [&](int t) { return (t < sink_n ? t : win_0 + (t - sink_n)) * BN; };
+  bt.sink_n = (int)sink_t1;
+  bt.win_0 = (int)win_t0;
+  bt.ntl = (int)(sink_t1 + (win_t1 - win_t0));
+  return bt;
+}
 
-  // ---- per-lane softmax state (row qi; lanes l and l^32 share the row)
+// Online-softmax state and O accumulator of 32 query rows of one head.  Row n
+// is held by lanes n and n + 32: they split the scores of each 32-key block
+// of the S^T accumulator and the d columns of O^T.
+template <int D>
+struct Rows32 {
   f32x16 oacc[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
-  float m_run = -INFINITY;  // reference max, log2 units (scaled)
-  float l_run = 0.f;        // this lane's partial row sum
+  float m_run;  // reference max, log2 units (scaled)
+  float l_run;  // this lane's partial row sum
+  int64_t qi;   // this lane's row
+  int64_t qpos, qpos_min, qpos_max;
 
-  const int64_t wq_last = (wrow0 + 31 < p.n_q ? wrow0 + 31 : p.n_q - 1);
-  const int64_t wqpos_min = p.q_pos0 + wrow0;
-  const int64_t wqpos_max = p.q_pos0 + (wq_last >= wrow0 ? wq_last : wrow0);
-
-  // ---- staging and per-lane LDS read offsets
-  LdsCopy<D, NW, true> kcp;
-  LdsCopy<D, NW, false> vcp;
-  LdsCopyVT<D, NW> vtcp;
-  KRegStage<D, NW, KMODE == 0 ? 1 : KMODE> kreg;
-  if constexpr (KMODE == 0)
-    kcp.init(kbase, p.ks_s, p.n_kv, wave, lane);
-  else
-    kreg.init(p, kbase, tid);
-  if constexpr (VT)
-    vtcp.init(vbase, wave, lane);
-  else
-    vcp.init(vbase, p.vs_s, p.n_kv, wave, lane);
-  int koff[D / 16];
+  __device__ __forceinline__ void init(const AttnParams& p, int64_t row0, int l32) {
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) koff[c] = l32 * D + 8 * ((2 * c + h2) ^ k_swz<D>(l32));
-  int voff[4] = {0, 0, 0, 0};
-  if constexpr (VT) {
+    for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) voff[kc] = l32 * BN + 8 * ((2 * kc + h2) ^ vt_swz(l32));
-  } else {
-    const int i = lane & 15, gg = (lane >> 4) & 1;
-    const int r = 4 * h2 + (i >> 2);
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-      voff[db] = r * D + 8 * ((4 * db + 2 * gg + ((i & 3) >> 1)) ^ v_swz<D>(r)) + 4 * (i & 1);
+      for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
+    m_run = -INFINITY;
+    l_run = 0.f;
+    qi = row0 + l32;
+    qpos = p.q_pos0 + qi;
+    const int64_t last = (row0 + 31 < p.n_q ? row0 + 31 : p.n_q - 1);
+    qpos_min = p.q_pos0 + row0;
+    qpos_max = p.q_pos0 + (last >= row0 ? last : row0);
   }
-
-  // ---- per-tile pieces of the online softmax
-  // mask S(t) (only for tiles that straddle a mask edge for this wave)
-  auto mask_tile = [&](f32x16 (&s)[2], const int j0) {
+  // mask S(t) (only for tiles that straddle a mask edge for these rows)
+  __device__ __forceinline__ void mask(const AttnParams& p, f32x16 (&s)[2], int j0, int h2) const {
     const int64_t kpos_min = p.k_pos0 + j0;
     const int64_t kpos_max = p.k_pos0 + (j0 + BN <= p.n_kv ? j0 + BN : p.n_kv) - 1;
-    const bool all_kept = (j0 + BN <= p.n_kv) && (!p.causal || kpos_max <= wqpos_min) &&
-                          (p.window < 0 || kpos_min >= wqpos_max - p.window ||
+    const bool all_kept = (j0 + BN <= p.n_kv) && (!p.causal || kpos_max <= qpos_min) &&
+                          (p.window < 0 || kpos_min >= qpos_max - p.window ||
                            kpos_max < (int64_t)p.n_sink);
     if (!all_kept) {
       // Branch-free, in 32-bit offsets within the tile: key at offset `off`
@@ -485,18 +449,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
           s[kb][r] = ok ? s[kb][r] : -INFINITY;
         }
     }
-  };
+  }
   // row max of a score tile, in scaled log2 units, shared by lanes l and l^32
-  auto tile_max = [&](const f32x16 (&s)[2]) {
+  __device__ __forceinline__ float tile_max(const AttnParams& p, const f32x16 (&s)[2]) const {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     return xor32_max(mx) * p.scale_log2;
-  };
+  }
   // move the reference max when the row max grew by more than 2^kLazyTau
-  auto rescale = [&](const float mx) {
+  __device__ __forceinline__ void rescale(float mx) {
     const float m_new = fmaxf(m_run, mx);
     if (__any(m_new > m_run + kLazyTau)) {
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -507,11 +471,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
     }
-  };
-  // P = exp2(S·scale - m) in bf16, row sums, O^T += V^T P^T
-  auto exp_pv = [&](const f32x16 (&s)[2], const uint16_t* vt) {
+  }
+  // P = exp2(S·scale - m) in bf16 (the B operand of PV) and the row sums
+  __device__ __forceinline__ void probs(const AttnParams& p, const f32x16 (&s)[2], bf16x8 (&pf)[4]) {
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    bf16x8 pf[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float pv[16];
@@ -528,23 +491,146 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
         pf[kb * 2 + hlf] = __builtin_bit_cast(bf16x8, w);
       }
     }
+  }
+  // epilogue: O = O_acc / l, LSE = ln 2 · (m + log2 l); o_mode 2 merges into
+  // the existing (O, LSE) partial
+  __device__ __forceinline__ void store(const AttnParams& p, int b, int hq, int h2) const {
+    const float l_tot = xor32_sum(l_run);
+    if (qi >= p.n_q) return;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse_new = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
+    float* lse_ptr = p.lse + b * p.ls_b + hq * p.ls_h + qi;
+    if (p.o_mode == 0) {
+      uint16_t* op = static_cast<uint16_t*>(p.o) + b * p.os_b + hq * p.os_h + qi * p.os_s;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc)
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv_operand<D, VT>(vt, voff, db, kc), pf[kc],
-                                                           oacc[db], 0, 0, 0);
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d0 = db * 32 + r4 * 8 + h2 * 4;
+          u32x2 w = {pack_bf16x2(oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv),
+                     pack_bf16x2(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv)};
+          *reinterpret_cast<u32x2*>(op + d0) = w;
+        }
+      if (h2 == 0) *lse_ptr = lse_new;
+    } else if (p.o_mode == 1) {
+      float* op = static_cast<float*>(p.o) + b * p.os_b + hq * p.os_h + qi * p.os_s;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d0 = db * 32 + r4 * 8 + h2 * 4;
+          f32x4 w = {oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv, oacc[db][4 * r4 + 2] * inv,
+                     oacc[db][4 * r4 + 3] * inv};
+          *reinterpret_cast<f32x4*>(op + d0) = w;
+        }
+      if (h2 == 0) *lse_ptr = lse_new;
+    } else {
+      // merge into the existing partial: identity when either side is empty
+      float* op = static_cast<float*>(p.o) + b * p.os_b + hq * p.os_h + qi * p.os_s;
+      const float lse_old = *lse_ptr;
+      if (lse_new == -INFINITY) return;
+      float wa, wb, lse_m;
+      if (lse_old == -INFINITY) {
+        wa = 0.f;
+        wb = 1.f;
+        lse_m = lse_new;
+      } else {
+        const float mxl = fmaxf(lse_old, lse_new);
+        const float mnl = fminf(lse_old, lse_new);
+        lse_m = mxl + log1pf(expf(mnl - mxl));
+        wa = expf(lse_old - lse_m);
+        wb = expf(lse_new - lse_m);
+      }
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d0 = db * 32 + r4 * 8 + h2 * 4;
+          f32x4 old = *reinterpret_cast<const f32x4*>(op + d0);
+          f32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            w[e] = (lse_old == -INFINITY ? 0.f : wa * old[e]) + wb * (oacc[db][4 * r4 + e] * inv);
+          *reinterpret_cast<f32x4*>(op + d0) = w;
+        }
+      if (h2 == 0) *lse_ptr = lse_m;
     }
-  };
+  }
+};
 
-  // ---- the tile loop: step t computes tile t from stage t % NST while the
-  // copy of tile t + NST - 1 is in flight, then waits for its own copies of
-  // tile t + 1 and meets the other waves at the barrier (after which stage
-  // t % NST may be overwritten).  The loop is unrolled NST times so that every
-  // step names its stage arrays directly.
+// per-lane LDS read offsets of the QK^T (K) and PV (V) operands
+template <int D, bool VT>
+__device__ __forceinline__ void operand_offsets(int lane, int (&koff)[D / 16], int (&voff)[4]) {
+  const int l32 = lane & 31, h2 = lane >> 5;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) koff[c] = l32 * D + 8 * ((2 * c + h2) ^ k_swz<D>(l32));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) voff[i] = 0;
+  if constexpr (VT) {
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) voff[kc] = l32 * BN + 8 * ((2 * kc + h2) ^ vt_swz(l32));
+  } else {
+    const int i = lane & 15, gg = (lane >> 4) & 1;
+    const int r = 4 * h2 + (i >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+      voff[db] = r * D + 8 * ((4 * db + 2 * gg + ((i & 3) >> 1)) ^ v_swz<D>(r)) + 4 * (i & 1);
+  }
+}
+
+template <int D, int KMODE, int NW, bool VT>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnParams p) {
+  using T = Tile<D, NW>;
+  // Stages of (K, V) tiles in LDS, one array each so that every unrolled step
+  // names its stages directly.  Pre-rotated f16 K and V are copied straight
+  // to LDS, three stages deep; K converted on the way goes through registers,
+  // two stages.
+  constexpr int NST = KMODE == 0 ? 3 : 2;
+  constexpr int E3 = NST > 2 ? T::ELEMS : 8;
+  __shared__ __attribute__((aligned(1024))) uint16_t k_st0[T::ELEMS], k_st1[T::ELEMS], k_st2[E3];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_st0[T::ELEMS], v_st1[T::ELEMS], v_st2[E3];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int h2 = lane >> 5;
+
+  const BlockTiles bt = block_tiles<T::BM>(p);
+  const int ntl = bt.ntl;
+  const uint16_t* qbase = p.q + bt.b * p.qs_b + bt.hq * p.qs_h;
+  const uint16_t* kbase = p.k + bt.b * p.ks_b + bt.hkv * p.ks_h;
+  const uint16_t* vbase = p.v + bt.b * p.vs_b + bt.hkv * p.vs_h;
+
+  Rows32<D> rows;
+  rows.init(p, bt.row0 + wave * 32, l32);
+  // Q fragment (RoPE fused here when q_mode == 2)
+  f16x8 qf[D / 16];
+  load_q<D>(p, qbase, rows.qi, h2, qf);
+
+  // ---- staging and per-lane LDS read offsets
+  LdsCopy<D, NW, true> kcp;
+  LdsCopy<D, NW, false> vcp;
+  LdsCopyVT<D, NW> vtcp;
+  KRegStage<D, NW, KMODE == 0 ? 1 : KMODE> kreg;
+  if constexpr (KMODE == 0)
+    kcp.init(kbase, p.ks_s, p.n_kv, wave, lane);
+  else
+    kreg.init(p, kbase, tid);
+  if constexpr (VT)
+    vtcp.init(vbase, wave, lane);
+  else
+    vcp.init(vbase, p.vs_s, p.n_kv, wave, lane);
+  int koff[D / 16], voff[4];
+  operand_offsets<D, VT>(lane, koff, voff);
+
+  // ---- the tile loop: each step waits for its own copies of tile t + 1,
+  // then meets the other waves (after which stage t % NST may be
+  // overwritten); unrolled NST times so that every step names its stage
+  // arrays directly
   constexpr int kLoadsPerTile = KMODE == 0 ? 2 * T::LPW : T::LPW;  // vector memory ops per wave
   auto issue = [&](uint16_t* ks, uint16_t* vs, int t) {
-    const int j0 = tile_j0(t);
+    const int j0 = bt.j0(t);
     if constexpr (KMODE == 0) kcp.issue(ks, j0);
     if constexpr (VT)
       vtcp.issue(vs, j0);
@@ -556,14 +642,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     const int tn = t + NST - 1;
     const bool pre = tn < ntl;
     if (pre) {
-      if constexpr (KMODE != 0) kreg.load(tile_j0(tn));
+      if constexpr (KMODE != 0) kreg.load(bt.j0(tn));
       issue(ks_next, vs_next, tn);
     }
     f32x16 s_cur[2];
     qk_tile<D>(ks, koff, qf, s_cur);
-    mask_tile(s_cur, tile_j0(t));
-    rescale(tile_max(s_cur));
-    exp_pv(s_cur, vs);
+    rows.mask(p, s_cur, bt.j0(t), h2);
+    rows.rescale(rows.tile_max(p, s_cur));
+    bf16x8 pf[4];
+    rows.probs(p, s_cur, pf);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+        rows.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv_operand<D, VT>(vs, voff, db, kc), pf[kc],
+                                                                rows.oacc[db], 0, 0, 0);
     if constexpr (KMODE != 0) {
       if (pre) kreg.store(ks_next);
     }
@@ -575,14 +668,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
 
   if (ntl > 0) {
     if constexpr (KMODE != 0) {
-      kreg.load(tile_j0(0));
+      kreg.load(bt.j0(0));
       kreg.store(k_st0);
     }
     issue(k_st0, v_st0, 0);
   }
   if (NST > 2 && ntl > 1) issue(k_st1, v_st1, 1);
   // draining here costs one copy latency per workgroup and gives the loop a
-  // single entry state, in which the compiler can tell the stages apart
+  // single entry state
   stage_barrier<0>();
   for (int t = 0; t < ntl; t += NST) {
     if constexpr (NST > 2) {
@@ -598,66 +691,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     }
   }
 
-  // ---- epilogue: O = O_acc / l, LSE = ln 2 · (m + log2 l)
-  const float l_tot = xor32_sum(l_run);
-  if (qi >= p.n_q) return;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const float lse_new = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
-  float* lse_ptr = p.lse + b * p.ls_b + hq * p.ls_h + qi;
-
-  if (p.o_mode == 0) {
-    uint16_t* op = static_cast<uint16_t*>(p.o) + b * p.os_b + hq * p.os_h + qi * p.os_s;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d0 = db * 32 + r4 * 8 + h2 * 4;
-        u32x2 w = {pack_bf16x2(oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv),
-                   pack_bf16x2(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv)};
-        *reinterpret_cast<u32x2*>(op + d0) = w;
-      }
-    if (h2 == 0) *lse_ptr = lse_new;
-  } else if (p.o_mode == 1) {
-    float* op = static_cast<float*>(p.o) + b * p.os_b + hq * p.os_h + qi * p.os_s;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d0 = db * 32 + r4 * 8 + h2 * 4;
-        f32x4 w = {oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv, oacc[db][4 * r4 + 2] * inv,
-                   oacc[db][4 * r4 + 3] * inv};
-        *reinterpret_cast<f32x4*>(op + d0) = w;
-      }
-    if (h2 == 0) *lse_ptr = lse_new;
-  } else {
-    // merge into the existing partial: identity when either side is empty
-    float* op = static_cast<float*>(p.o) + b * p.os_b + hq * p.os_h + qi * p.os_s;
-    const float lse_old = *lse_ptr;
-    if (lse_new == -INFINITY) return;
-    float wa, wb, lse_m;
-    if (lse_old == -INFINITY) {
-      wa = 0.f; wb = 1.f; lse_m = lse_new;
-    } else {
-      const float mxl = fmaxf(lse_old, lse_new);
-      const float mnl = fminf(lse_old, lse_new);
-      lse_m = mxl + log1pf(expf(mnl - mxl));
-      wa = expf(lse_old - lse_m);
-      wb = expf(lse_new - lse_m);
-    }
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d0 = db * 32 + r4 * 8 + h2 * 4;
-        f32x4 old = *reinterpret_cast<const f32x4*>(op + d0);
-        f32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w[e] = (lse_old == -INFINITY ? 0.f : wa * old[e]) + wb * (oacc[db][4 * r4 + e] * inv);
-        *reinterpret_cast<f32x4*>(op + d0) = w;
-      }
-    if (h2 == 0) *lse_ptr = lse_m;
-  }
+  rows.store(p, bt.b, bt.hq, h2);
 }
 
 // Explicit instantiations: with only the implicit ones from launch_dn, the
