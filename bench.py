@@ -87,17 +87,110 @@ def copy_calibration(gib: float = 1.0, reps: int = 5):
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "reps": reps}))
 
 
+def bench_chunked(args, w):
+    """The million-token layer as the one-GPU share of ring attention: KV in
+    chunks of w.chunk keys, one attention call per chunk, partials merged by
+    LSE.  A step = tables + K rotation + V packing + the chunked driver with the
+    merge fused into each call's epilogue; the separate-merge form (attention
+    into a partial, then lcx_attn_merge) is timed once after the steps."""
+    import numpy as np
+    import torch
+
+    import fixtures
+    import long_context_attention_rope_amd as lcx
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q = to_dev(fixtures.normal_bf16(w.seed, fixtures.Q_ID, (w.B, w.Hq, w.n, w.d)))
+    k = to_dev(fixtures.normal_bf16(w.seed, fixtures.K_ID, (w.B, w.Hkv, w.n, w.d)))
+    v = to_dev(fixtures.normal_bf16(w.seed, fixtures.V_ID, (w.B, w.Hkv, w.n, w.d)))
+    cfg = lcx.rope_cfg(w.scheme, w.base, w.d, w.L_train, w.L_target, w.cur_len, w.alpha, w.beta)
+    cos = torch.empty((w.n, w.d // 2), dtype=torch.float32, device=dev)
+    sin = torch.empty_like(cos)
+    k_rot = torch.empty(k.shape, dtype=torch.float16, device=dev)
+    v_tiles = torch.empty((w.B, w.Hkv, (w.n + 63) // 64, w.d, 64), dtype=torch.bfloat16, device=dev)
+    acc_o = torch.empty((w.B, w.Hq, w.n, w.d), dtype=torch.float32, device=dev)
+    acc_l = torch.empty((w.B, w.Hq, w.n), dtype=torch.float32, device=dev)
+    o = torch.empty((w.B, w.Hq, w.n, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.Hq, w.n), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None, o_part=None, lse_part=None):
+        if ev: ev[0].record(stream)
+        lcx.rope_freqs(cfg, cos, sin, 0)
+        lcx.rope_apply_qk(None, k, cos, sin, k_out=k_rot)
+        lcx.pack_v(v, out=v_tiles)
+        if ev: ev[1].record(stream)
+        lcx.attn_fwd_chunked(q, k_rot, v_tiles, w.chunk, acc_o, acc_l, o, lse, o_part=o_part,
+                             lse_part=lse_part, rope_q=True, cos=cos, sin=sin, rope=cfg)
+        if ev: ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    drv_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    # separate merge pass, timed once
+    o_part = torch.empty_like(acc_o)
+    lse_part = torch.empty_like(acc_l)
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    step(sev, o_part, lse_part)
+    torch.cuda.synchronize()
+    sep_ms = sev[1].elapsed_time(sev[2])
+
+    flop = w.flop()
+    ms_step = wall * 1e3 / args.steps
+    drv_tflops = flop / (drv_ms * 1e-3) / 1e12
+    n_chunks = (w.n + w.chunk - 1) // w.chunk
+    out = {
+        "metric": "causal attn TFLOP/s, 1M-token GQA layer as 128 KV chunks + LSE merge (one GPU's ring share)",
+        "value": round(flop / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
+                   "seq_len": w.n, "rope": w.scheme, "rope_base": w.base, "L_train": w.L_train,
+                   "L_target": w.L_target, "causal": True, "kv_chunk": w.chunk, "chunks": n_chunks,
+                   "merge": "fused into each chunk's epilogue (accumulate)", "v_layout": "tiles"},
+        "pct_bf16_peak": round(100 * flop / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "tokens_per_s": round(w.B * w.n / (ms_step * 1e-3), 1),
+        "kernels_ms": {"tables_rotate_pack": round(prep_ms, 3), "chunked_attention_fused_merge": round(drv_ms, 1),
+                       "chunked_attention_separate_merge": round(sep_ms, 1)},
+        "roofline": {"kernel": "attn_fwd (128 chunk launches)", "bound": "mfma", "achieved": round(drv_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(drv_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }
+    if args.cpu_rows > 0:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 10; 1 for the chunked workload)")
+    ap.add_argument("--warmup", type=int, default=None, help="warm-up steps (default 3; 1 for the chunked workload)")
     ap.add_argument("--workload", default="llama3_70b_128k_dynntk")
     ap.add_argument("--k-mode", choices=["prerotate", "fused"], default="prerotate",
                     help="K rotated once by lcx_rope_apply_qk (default) or inside the attention tile load")
     ap.add_argument("--v-layout", choices=["tiles", "rows"], default="tiles",
                     help="V packed into 64-key tiles by lcx_attn_pack_v inside the step (default) or read as rows")
-    ap.add_argument("--cpu-rows", type=int, default=2048, help="oracle rows for the CPU baseline (0: skip)")
+    ap.add_argument("--cpu-rows", type=int, default=None,
+                    help="oracle rows for the CPU baseline (default 2048; 640 for the chunked workload; 0: skip)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-merge-check", dest="merge_check", action="store_false",
                     help="skip timing the merge pass on this layer's partial sizes")
@@ -120,8 +213,14 @@ def main():
     from fixtures import workloads as W
 
     w = W.BY_NAME[args.workload]
+    if args.steps is None:
+        args.steps = 1 if w.chunk else 10
+    if args.warmup is None:
+        args.warmup = 1 if w.chunk else 3
+    if args.cpu_rows is None:
+        args.cpu_rows = 640 if w.chunk else 2048
     if w.chunk:
-        raise SystemExit("bench.py times single-call workloads; the chunked one is a parity case")
+        return bench_chunked(args, w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
