@@ -18,7 +18,7 @@ class Workload:
     Hkv: int
     d: int
     n: int
-    scheme: str           # plain | pi | ntk | ntk_parts | yarn | dynamic_ntk
+    scheme: str           # plain | pi | ntk | ntk_parts | yarn | dynamic_ntk | pair_factors
     base: float
     L_train: int
     L_target: int
@@ -30,6 +30,7 @@ class Workload:
     n_sink: int = 0
     chunk: int = 0        # >0: KV processed in chunks of this many keys + merge
     seed: int = 1
+    factors: tuple = None # pair_factors: the d/2 per-pair frequency divisors
 
     @property
     def s(self) -> float:

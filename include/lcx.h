@@ -55,7 +55,8 @@ typedef enum {
   LCX_ROPE_NTK = 3,
   LCX_ROPE_NTK_PARTS = 4,
   LCX_ROPE_YARN = 5,
-  LCX_ROPE_DYNAMIC_NTK = 6
+  LCX_ROPE_DYNAMIC_NTK = 6,
+  LCX_ROPE_PAIR_FACTORS = 7 /* theta'_i = theta_i / factors[i]  [CW §2.5 LongRoPE] */
 } lcx_rope_scheme;
 
 typedef enum { LCX_BF16 = 0, LCX_F32 = 1, LCX_F16 = 2 } lcx_dtype;
@@ -72,6 +73,8 @@ typedef struct {
   int64_t cur_len;  /* DYNAMIC_NTK: current length l; 0 means L_target */
   double alpha;     /* NTK_PARTS / YARN: 0 < alpha < beta (pages: 1) */
   double beta;      /* (pages: 32) */
+  const double* factors; /* PAIR_FACTORS: d/2 finite factors > 0, one per rotation plane
+                            (host memory, read during the call); ignored otherwise */
 } lcx_rope_cfg;
 
 /*

@@ -22,7 +22,8 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
-SCHEMES = {"none": 0, "plain": 1, "pi": 2, "ntk": 3, "ntk_parts": 4, "yarn": 5, "dynamic_ntk": 6}
+SCHEMES = {"none": 0, "plain": 1, "pi": 2, "ntk": 3, "ntk_parts": 4, "yarn": 5, "dynamic_ntk": 6,
+           "pair_factors": 7}
 BF16, F32, F16 = 0, 1, 2
 _DT = {torch.bfloat16: BF16, torch.float32: F32, torch.float16: F16}
 
@@ -31,7 +32,8 @@ _i32, _i64, _f64, _f32, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_double, c
 
 class RopeCfg(ctypes.Structure):
     _fields_ = [("scheme", _i32), ("head_dim", _i32), ("base", _f64), ("L_train", _i64),
-                ("L_target", _i64), ("cur_len", _i64), ("alpha", _f64), ("beta", _f64)]
+                ("L_target", _i64), ("cur_len", _i64), ("alpha", _f64), ("beta", _f64),
+                ("factors", ctypes.POINTER(_f64))]
 
 
 class AttnArgs(ctypes.Structure):
@@ -99,8 +101,15 @@ def _s2(t):
 
 
 def rope_cfg(scheme: str, base: float, head_dim: int, L_train: int = 1, L_target: int = 1,
-             cur_len: int = 0, alpha: float = 1.0, beta: float = 32.0) -> RopeCfg:
-    return RopeCfg(SCHEMES[scheme], head_dim, base, L_train, L_target, cur_len, alpha, beta)
+             cur_len: int = 0, alpha: float = 1.0, beta: float = 32.0, factors=None) -> RopeCfg:
+    """factors: the d/2 per-pair factors of the pair_factors scheme (copied here and
+    kept alive with the returned struct)."""
+    cfg = RopeCfg(SCHEMES[scheme], head_dim, base, L_train, L_target, cur_len, alpha, beta, None)
+    if factors is not None:
+        arr = (_f64 * len(factors))(*[float(x) for x in factors])
+        cfg._factors_keep = arr
+        cfg.factors = ctypes.cast(arr, ctypes.POINTER(_f64))
+    return cfg
 
 
 def rope_freqs(cfg: RopeCfg, cos: torch.Tensor | None = None, sin: torch.Tensor | None = None,

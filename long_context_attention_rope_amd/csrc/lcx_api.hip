@@ -39,7 +39,7 @@ bool is_scaling(int32_t scheme) {
 
 lcx_status check_cfg(const lcx_rope_cfg* c) {
   if (!c) return fail(LCX_ERR_INVALID_ARG, "rope cfg is NULL");
-  if (c->scheme < LCX_ROPE_PLAIN || c->scheme > LCX_ROPE_DYNAMIC_NTK)
+  if (c->scheme < LCX_ROPE_PLAIN || c->scheme > LCX_ROPE_PAIR_FACTORS)
     return fail(LCX_ERR_INVALID_ARG, "rope scheme %d is not a scheme with frequencies", c->scheme);
   if (c->head_dim < 2 || (c->head_dim & 1))
     return fail(LCX_ERR_INVALID_ARG, "head_dim %d must be even and >= 2", c->head_dim);
@@ -56,6 +56,12 @@ lcx_status check_cfg(const lcx_rope_cfg* c) {
   if ((c->scheme == LCX_ROPE_NTK_PARTS || c->scheme == LCX_ROPE_YARN) &&
       !(c->alpha > 0.0 && c->alpha < c->beta && std::isfinite(c->beta)))
     return fail(LCX_ERR_INVALID_ARG, "need 0 < alpha (%g) < beta (%g)", c->alpha, c->beta);
+  if (c->scheme == LCX_ROPE_PAIR_FACTORS) {
+    if (!c->factors) return fail(LCX_ERR_INVALID_ARG, "PAIR_FACTORS needs factors[d/2]");
+    for (int i = 0; i < c->head_dim / 2; ++i)
+      if (!(c->factors[i] > 0.0) || !std::isfinite(c->factors[i]))
+        return fail(LCX_ERR_INVALID_ARG, "factors[%d] = %g must be finite and > 0", i, c->factors[i]);
+  }
   return LCX_OK;
 }
 
@@ -67,7 +73,9 @@ lcx_status check_cfg(const lcx_rope_cfg* c) {
 // wavelength 2π/theta_i: 1 below L_train/beta, 1/s above L_train/alpha,
 // linear in the wavelength in between (continuous at both ends); YaRN (§2.4)
 // adds the logit divisor t = 0.1·ln s + 1; PI (§2.1) scales positions by
-// L_train/L_target instead of touching the frequencies.
+// L_train/L_target instead of touching the frequencies; per-pair factors
+// (LongRoPE, §2.5: one factor per rotation plane, found by a search that is
+// not part of this library) divide each pair's frequency by its factor.
 void scheme_freqs(const lcx_rope_cfg& c, double* theta, double* pos_factor, double* logit_mult) {
   const int d = c.head_dim;
   const double s = is_scaling(c.scheme) ? (double)c.L_target / (double)c.L_train : 1.0;
@@ -95,6 +103,8 @@ void scheme_freqs(const lcx_rope_cfg& c, double* theta, double* pos_factor, doub
       theta[i] *= f;
     }
   }
+  if (c.scheme == LCX_ROPE_PAIR_FACTORS)
+    for (int i = 0; i < d / 2; ++i) theta[i] /= c.factors[i];
   *pos_factor = c.scheme == LCX_ROPE_PI ? (double)c.L_train / (double)c.L_target : 1.0;
   *logit_mult = c.scheme == LCX_ROPE_YARN ? 1.0 / (0.1 * std::log(s) + 1.0) : 1.0;
 }

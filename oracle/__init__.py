@@ -21,7 +21,8 @@ _lock = threading.Lock()
 _lib = None
 
 # the oracle's own scheme ids (independent of the GPU library's enum)
-SCHEMES = {"none": 0, "plain": 1, "pi": 2, "ntk": 3, "ntk_parts": 4, "yarn": 5, "dynamic_ntk": 6}
+SCHEMES = {"none": 0, "plain": 1, "pi": 2, "ntk": 3, "ntk_parts": 4, "yarn": 5, "dynamic_ntk": 6,
+           "pair_factors": 7}
 
 
 def build(force: bool = True) -> str:
@@ -46,7 +47,7 @@ def _load():
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = ctypes.c_int
             lib.oracle_rope_freqs.argtypes = [ctypes.c_int, f64, ctypes.c_int, i64, i64, i64, f64, f64,
-                                              vp, vp, vp]
+                                              vp, vp, vp, vp]
             lib.oracle_rope_freqs.restype = ctypes.c_int
             lib.oracle_rope_table.argtypes = [vp, ctypes.c_int, f64, i64, i64, vp, vp]
             lib.oracle_rope_table.restype = None
@@ -70,14 +71,19 @@ def _c(a, dtype):
 
 
 def rope_freqs(scheme: str, base: float, d: int, L_train: int = 1, L_target: int = 1,
-               cur_len: int = 0, alpha: float = 1.0, beta: float = 32.0):
-    """(theta'[d/2], position factor, logit multiplier) — step a1."""
+               cur_len: int = 0, alpha: float = 1.0, beta: float = 32.0, factors=None):
+    """(theta'[d/2], position factor, logit multiplier) — step a1.  factors: the
+    d/2 per-pair factors of the pair_factors scheme."""
     lib = _load()
     theta = np.zeros(d // 2, dtype=np.float64)
     pf = ctypes.c_double(0.0)
     lm = ctypes.c_double(0.0)
+    fac = None if factors is None else _c(factors, np.float64)
+    if fac is not None and fac.shape != (d // 2,):
+        raise ValueError("factors must hold d/2 values")
     rc = lib.oracle_rope_freqs(SCHEMES[scheme], float(base), int(d), int(L_train), int(L_target),
-                               int(cur_len), float(alpha), float(beta), theta.ctypes.data,
+                               int(cur_len), float(alpha), float(beta),
+                               fac.ctypes.data if fac is not None else None, theta.ctypes.data,
                                ctypes.addressof(pf), ctypes.addressof(lm))
     if rc != 0:
         raise ValueError("oracle_rope_freqs: invalid arguments")

@@ -60,7 +60,8 @@ enum {
   OR_NTK = 3,
   OR_NTK_PARTS = 4,
   OR_YARN = 5,
-  OR_DYNAMIC_NTK = 6
+  OR_DYNAMIC_NTK = 6,
+  OR_PAIR_FACTORS = 7
 };
 
 static const double OR_PI_CONST = 3.14159265358979323846264338327950288;
@@ -104,18 +105,30 @@ static void plain_theta(double base, int d, double* theta) {
  *                concept page's "multiply by 1/√t" is not used).
  *   DYNAMIC_NTK  l = cur_len (0 means L_target); base' = base when
  *                l <= L_train, else base·(l/L_train)^(d/(d-2)).       [CW §3]
+ *   PAIR_FACTORS theta'_i = theta_i / factors[i], factor 1, multiplier 1.
+ *                                                                     [CW §2.5]
+ *                READING: the page gives LongRoPE one scale factor per 2-D
+ *                rotation plane, chosen by a search; the factor divides that
+ *                plane's frequency the way PI's s divides all of them (all
+ *                factors = s reproduces PI's angles).  The search is not
+ *                part of the path: the factors are an input.
  *
  * s = L_target / L_train.  Returns 0, or -1 for arguments outside the
  * definitions (d odd or < 2, base <= 1, L_train <= 0, L_target < L_train
  * for the scaling schemes, alpha >= beta or alpha <= 0 for the ramp).
  */
 int oracle_rope_freqs(int scheme, double base, int d, int64_t L_train, int64_t L_target,
-                      int64_t cur_len, double alpha, double beta, double* theta,
-                      double* pos_factor, double* logit_mult) {
+                      int64_t cur_len, double alpha, double beta, const double* factors,
+                      double* theta, double* pos_factor, double* logit_mult) {
   if (d < 2 || (d & 1) || !(base > 1.0)) return -1;
   int scaled = (scheme == OR_PI || scheme == OR_NTK || scheme == OR_NTK_PARTS ||
                 scheme == OR_YARN || scheme == OR_DYNAMIC_NTK);
-  if (scheme < OR_PLAIN || scheme > OR_DYNAMIC_NTK) return -1;
+  if (scheme < OR_PLAIN || scheme > OR_PAIR_FACTORS) return -1;
+  if (scheme == OR_PAIR_FACTORS) {
+    if (!factors) return -1;
+    for (int i = 0; i < d / 2; ++i)
+      if (!(factors[i] > 0.0) || !isfinite(factors[i])) return -1;
+  }
   if (scaled && (L_train <= 0 || L_target < L_train)) return -1;
   if ((scheme == OR_NTK_PARTS || scheme == OR_YARN) && !(alpha > 0.0 && alpha < beta)) return -1;
 
@@ -166,6 +179,10 @@ int oracle_rope_freqs(int scheme, double base, int d, int64_t L_train, int64_t L
       plain_theta(b2, d, theta);
       break;
     }
+    case OR_PAIR_FACTORS:
+      plain_theta(base, d, theta);
+      for (int i = 0; i < d / 2; ++i) theta[i] = theta[i] / factors[i];
+      break;
   }
   if (pos_factor) *pos_factor = factor;
   if (logit_mult) *logit_mult = mult;

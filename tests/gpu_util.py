@@ -42,7 +42,8 @@ def inputs(w, n_q=None, n_kv=None):
 
 
 def oracle_freqs(w):
-    return oracle.rope_freqs(w.scheme, w.base, w.d, w.L_train, w.L_target, w.cur_len, w.alpha, w.beta)
+    return oracle.rope_freqs(w.scheme, w.base, w.d, w.L_train, w.L_target, w.cur_len, w.alpha, w.beta,
+                             factors=w.factors)
 
 
 def sample_rows(w, count=4096, seed=0, n_q=None, extra_pos=()):

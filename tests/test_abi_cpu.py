@@ -73,6 +73,24 @@ def test_host_scheme_math_matches_oracle(lcx, scheme, base, d, Lt, Lg, cur):
     assert pf == pytest.approx(pf_o, rel=1e-15) and lm == pytest.approx(lm_o, rel=1e-15)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_host_pair_factors_match_oracle(lcx, d):
+    f = np.exp(np.random.default_rng(d).uniform(0.0, np.log(64.0), d // 2))
+    th, pf, lm = lcx.rope_freqs(lcx.rope_cfg("pair_factors", 500000.0, d, factors=f))
+    th_o, pf_o, lm_o = oracle.rope_freqs("pair_factors", 500000.0, d, factors=f)
+    np.testing.assert_allclose(np.array(th), th_o, rtol=1e-15, atol=0)
+    assert pf == pf_o == 1.0 and lm == lm_o == 1.0
+
+
+def test_pair_factors_rejected(lcx):
+    _st(lcx, lcx.ERR_INVALID_ARG, lambda: lcx.rope_freqs(lcx.rope_cfg("pair_factors", 10000.0, 64)))
+    f = np.ones(32)
+    f[5] = 0.0
+    _st(lcx, lcx.ERR_INVALID_ARG, lambda: lcx.rope_freqs(lcx.rope_cfg("pair_factors", 10000.0, 64, factors=f)))
+    f[5] = float("inf")
+    _st(lcx, lcx.ERR_INVALID_ARG, lambda: lcx.rope_freqs(lcx.rope_cfg("pair_factors", 10000.0, 64, factors=f)))
+
+
 def test_yarn_8b_softmax_constants(lcx):
     # the Llama-3-8B-shaped workload: s = 4, t = 0.1 ln 4 + 1
     _, _, lm = lcx.rope_freqs(lcx.rope_cfg("yarn", 500000.0, 128, 8192, 32768))

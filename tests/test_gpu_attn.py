@@ -22,7 +22,8 @@ def lcx():
 
 
 def _cfg(lcx, w):
-    return lcx.rope_cfg(w.scheme, w.base, w.d, w.L_train, w.L_target, w.cur_len, w.alpha, w.beta)
+    return lcx.rope_cfg(w.scheme, w.base, w.d, w.L_train, w.L_target, w.cur_len, w.alpha, w.beta,
+                        factors=w.factors)
 
 
 def _run(lcx, w, q, k, v, *, k_mode="pre_f16", out_dtype=torch.bfloat16, q_pos0=0, k_pos0=0,
@@ -104,13 +105,21 @@ SMALL = [
     ("win0_sink3", 2, 1, 64, 300, "ntk", 0, 3, 1),
     ("win_big", 4, 2, 128, 520, "yarn", 64, 0, 1),
     ("win_tiles", 4, 2, 64, 1000, "plain", 127, 70, 1),
+    ("pairs_d128", 4, 1, 128, 400, "pair_factors", -1, 0, 1),
+    ("pairs_d64_win", 4, 2, 64, 300, "pair_factors", 50, 2, 1),
 ]
+
+
+def _pair_factors(d, seed):
+    # per-plane factors between 1 and 64, as a LongRoPE search might return
+    return tuple(np.exp(np.random.default_rng(seed).uniform(0.0, np.log(64.0), d // 2)))
 
 
 @pytest.mark.parametrize("name,Hq,Hkv,d,n,scheme,window,n_sink,B", SMALL)
 def test_small_shapes_full(lcx, name, Hq, Hkv, d, n, scheme, window, n_sink, B):
     w = W.Workload(name, B, Hq, Hkv, d, n, scheme, 10000.0 if d == 64 else 500000.0, 64, 256,
-                   cur_len=256, window=window, n_sink=n_sink, seed=100 + n)
+                   cur_len=256, window=window, n_sink=n_sink, seed=100 + n,
+                   factors=_pair_factors(d, n) if scheme == "pair_factors" else None)
     q, k, v = U.inputs(w)
     o_ref, l_ref = _all(w, q, k, v)
     for k_mode, v_tiled in (("pre_f16", False), ("pre_f16", True), ("fused", False), ("fused", True)):
@@ -195,7 +204,9 @@ def test_deterministic_and_every_output_written(lcx):
 
 
 def test_rope_tables_match_oracle(lcx):
-    for w in W.ALL:
+    pairs = W.LLAMA70B_128K.with_(name="70b_pair_factors", scheme="pair_factors",
+                                  factors=_pair_factors(128, 7))
+    for w in list(W.ALL) + [pairs]:
         cfg = _cfg(lcx, w)
         th, pf, _ = U.oracle_freqs(w)
         ranges = [(0, 2048), (max(0, w.n - 2048), w.n)]

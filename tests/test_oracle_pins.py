@@ -106,6 +106,28 @@ def test_ntk_by_parts_is_continuous():
     assert np.max(np.abs(np.diff(r))) < 0.03
 
 
+def test_pair_factors_reduce_to_plain_pi_and_by_parts():
+    # [CW §2.5]: one factor per rotation plane dividing that plane's frequency.
+    d, base, L, s = 128, 500000.0, 8192, 16
+    th_plain = plain(d, base)
+    th, pf, lm = oracle.rope_freqs("pair_factors", base, d, factors=np.ones(d // 2))
+    assert np.array_equal(th, th_plain) and pf == 1.0 and lm == 1.0
+    # all factors s: the angles of PI (positions scaled by 1/s), up to rounding
+    th_s, _, _ = oracle.rope_freqs("pair_factors", base, d, factors=np.full(d // 2, float(s)))
+    _, pf_pi, _ = oracle.rope_freqs("pi", base, d, L, L * s)
+    c1, s1 = oracle.rope_table(th_s, d, 1.0, 0, 4096)
+    c2, s2 = oracle.rope_table(th_plain, d, pf_pi, 0, 4096)
+    assert np.max(np.abs(c1 - c2)) < 1e-12 and np.max(np.abs(s1 - s2)) < 1e-12
+    # the by-parts ramp written as per-plane factors gives NTK-by-parts back
+    th_bp, _, _ = oracle.rope_freqs("ntk_parts", base, d, L, L * s)
+    th_f, _, _ = oracle.rope_freqs("pair_factors", base, d, factors=th_plain / th_bp)
+    np.testing.assert_allclose(th_f, th_bp, rtol=1e-15, atol=0)
+    # a factor that is not finite and > 0, or the wrong count, is rejected
+    for bad in (np.zeros(d // 2), np.full(d // 2, -2.0), np.full(d // 2, np.nan), np.ones(d // 2 - 1), None):
+        with pytest.raises(ValueError):
+            oracle.rope_freqs("pair_factors", base, d, factors=bad)
+
+
 def test_yarn_is_by_parts_plus_temperature():
     th_y, pf, lm = oracle.rope_freqs("yarn", 500000.0, 128, 8192, 32768)
     th_p, _, _ = oracle.rope_freqs("ntk_parts", 500000.0, 128, 8192, 32768)
