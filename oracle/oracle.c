@@ -27,7 +27,9 @@
  *                       at 1 and 1/s, continuous, monotone; dynamic = base
  *                       for l <= L_train and = NTK-aware(l/L_train) above;
  *                       geometric frequency ladder with ratio base^(-2/d);
- *                       PI 4K->8K position factor 0.5 (golden file).
+ *                       PI 4K->8K position factor 0.5 (golden file);
+ *                       per-pair factors: all 1 = plain, all s = PI's
+ *                       angles, by-parts ratios = NTK-by-parts.
  *                       The NTK-by-parts ramp interior and the YaRN
  *                       temperature direction have no printed value:
  *                       parity unpinned for those two readings.
