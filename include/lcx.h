@@ -157,6 +157,30 @@ typedef struct {
 lcx_status lcx_attn_fwd(const lcx_attn_args* a, hipStream_t stream);
 
 /*
+ * Decode over a long KV cache (split-KV): n_q <= 8 new query rows at
+ * positions q_pos0 .. q_pos0+n_q-1 (usually the last positions) against the
+ * cache keys k_pos0 .. k_pos0+n_kv-1, with the same mask rules as
+ * lcx_attn_fwd.  The KV tiles the rows visit are divided among n_splits
+ * workgroups per KV head; each writes a partial (O, LSE) into the caller's
+ * workspace and a combine pass merges them by log-sum-exp into o and lse.
+ * [CW §3 动态 NTK: the step's base, from the current length, is applied to
+ * the new rows through the tables; the cache keeps the rotation it was
+ * written with.  CW §5.3: merge of partial results by LSE.]
+ *   a         as for lcx_attn_fwd, with: k pre-rotated f16 (rope_k = 0,
+ *             k_dtype = LCX_F16); v rows or tiles (v_tiled); accumulate = 0;
+ *             (Hq/Hkv)·n_q <= 64.
+ *   n_splits  1 .. 65535 workgroups per KV head (splits with no tile write
+ *             an empty partial).
+ *   o_part    fp32 [n_splits][B][Hq][n_q][d], lse_part fp32
+ *             [n_splits][B][Hq][n_q]: caller-owned workspace, overwritten.
+ * Errors: as lcx_attn_fwd, plus INVALID_ARG for n_splits out of range, a NULL
+ * workspace or accumulate = 1; UNSUPPORTED for n_q > 8, (Hq/Hkv)·n_q > 64, K
+ * not pre-rotated f16, B or Hkv > 65535.
+ */
+lcx_status lcx_attn_decode(const lcx_attn_args* a, int32_t n_splits, float* o_part, float* lse_part,
+                           hipStream_t stream);
+
+/*
  * Layout step for the PV product (V is not transformed): V copied into the
  * tile layout that lcx_attn_fwd reads with v_tiled = 1, so that each MFMA
  * operand of O += P·V is one 16-byte LDS read (the same role as the

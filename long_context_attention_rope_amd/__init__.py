@@ -67,6 +67,8 @@ _lib.lcx_attn_merge.restype = ctypes.c_int
 _lib.lcx_attn_fwd_chunked.argtypes = [ctypes.POINTER(AttnArgs), _i64, _vp, _vp, _vp, _vp, _vp]
 _lib.lcx_attn_fwd_chunked.restype = ctypes.c_int
 _lib.lcx_attn_pack_v.argtypes = [_vp, _vp, _i32, _i32, _i64, _i32, _P3, _vp]
+_lib.lcx_attn_decode.argtypes = [ctypes.POINTER(AttnArgs), _i32, _vp, _vp, _vp]
+_lib.lcx_attn_decode.restype = ctypes.c_int
 _lib.lcx_attn_pack_v.restype = ctypes.c_int
 
 
@@ -217,6 +219,31 @@ def attn_fwd(q, k, v, o=None, lse=None, *, rope_q=False, rope_k=False, cos=None,
                    n_sink=n_sink, q_pos0=q_pos0, k_pos0=k_pos0, accumulate=accumulate,
                    causal=causal)
     _check(_lib.lcx_attn_fwd(ctypes.byref(a), _stream(q)))
+    return o, lse
+
+
+def attn_decode(q, k, v, o=None, lse=None, *, n_splits=None, o_part=None, lse_part=None,
+                rope_q=False, cos=None, sin=None, tab_pos0=0, rope=None, softmax_scale=0.0, window=-1,
+                n_sink=0, q_pos0=0, k_pos0=0, out_dtype=torch.bfloat16):
+    """lcx_attn_decode.  q [B,Hq,n_q<=8,d], k pre-rotated f16 [B,Hkv,n_kv,d], v rows or
+    pack_v tiles.  n_splits defaults to about 512 workgroups over B·Hkv, at most one per
+    4 KV tiles.  Returns (o, lse)."""
+    B, Hq, n_q, d = q.shape
+    Hkv, n_kv = k.shape[1], k.shape[2]
+    if n_splits is None:
+        n_splits = max(1, min(-(-512 // (B * Hkv)), n_kv // 256))
+    if o is None:
+        o = torch.empty((B, Hq, n_q, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, n_q), dtype=torch.float32, device=q.device)
+    if o_part is None:
+        o_part = torch.empty((n_splits, B, Hq, n_q, d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((n_splits, B, Hq, n_q), dtype=torch.float32, device=q.device)
+    a = _attn_args(q, k, v, o, lse, rope_q=rope_q, rope_k=False, cos=cos, sin=sin,
+                   tab_pos0=tab_pos0, cfg=rope, softmax_scale=softmax_scale, window=window,
+                   n_sink=n_sink, q_pos0=q_pos0, k_pos0=k_pos0, accumulate=False)
+    _check(_lib.lcx_attn_decode(ctypes.byref(a), n_splits, _ptr(o_part), _ptr(lse_part), _stream(q)))
     return o, lse
 
 

@@ -349,6 +349,9 @@ struct BlockTiles {
   __device__ __forceinline__ int j0(int t) const { return (t < sink_n ? t : win_0 + (t - sink_n)) * BN; }
 };
 
+__device__ __forceinline__ void tile_range(const AttnParams& p, int64_t qpos_min, int64_t qpos_max,
+                                           BlockTiles& bt);
+
 template <int BM>
 __device__ __forceinline__ BlockTiles block_tiles(const AttnParams& p) {
   BlockTiles bt;
@@ -370,10 +373,15 @@ __device__ __forceinline__ BlockTiles block_tiles(const AttnParams& p) {
   const int qblk = p.n_qblk - 1 - qrank;
   bt.hq = bt.hkv * p.G + g;
   bt.row0 = (int64_t)qblk * BM;
-
   const int64_t blk_last = (bt.row0 + BM < p.n_q ? bt.row0 + BM : p.n_q) - 1;
-  const int64_t qpos_min = p.q_pos0 + bt.row0;
-  const int64_t qpos_max = p.q_pos0 + blk_last;
+  tile_range(p, p.q_pos0 + bt.row0, p.q_pos0 + blk_last, bt);
+  return bt;
+}
+
+// the KV tiles that query positions [qpos_min, qpos_max] visit: optional sink
+// tiles, then the window / causal range
+__device__ __forceinline__ void tile_range(const AttnParams& p, int64_t qpos_min, int64_t qpos_max,
+                                           BlockTiles& bt) {
   int64_t j_hi = p.n_kv;
   if (p.causal) {
     const int64_t lim = qpos_max - p.k_pos0 + 1;
@@ -397,7 +405,6 @@ __device__ __forceinline__ BlockTiles block_tiles(const AttnParams& p) {
   bt.sink_n = (int)sink_t1;
   bt.win_0 = (int)win_t0;
   bt.ntl = (int)(sink_t1 + (win_t1 - win_t0));
-  return bt;
 }
 
 // Online-softmax state and O accumulator of 32 query rows of one head.  Row n
@@ -423,6 +430,21 @@ struct Rows32 {
     const int64_t last = (row0 + 31 < p.n_q ? row0 + 31 : p.n_q - 1);
     qpos_min = p.q_pos0 + row0;
     qpos_max = p.q_pos0 + (last >= row0 ? last : row0);
+  }
+  // lane row qi (>= n_q: no row) of a group whose kept positions span
+  // [qpos_lo, qpos_hi]
+  __device__ __forceinline__ void init_row(const AttnParams& p, int64_t row, int64_t qpos_lo,
+                                           int64_t qpos_hi) {
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
+    m_run = -INFINITY;
+    l_run = 0.f;
+    qi = row;
+    qpos = p.q_pos0 + row;
+    qpos_min = qpos_lo;
+    qpos_max = qpos_hi;
   }
   // mask S(t) (only for tiles that straddle a mask edge for these rows)
   __device__ __forceinline__ void mask(const AttnParams& p, f32x16 (&s)[2], int j0, int h2) const {
@@ -694,6 +716,101 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
   rows.store(p, bt.b, bt.hq, h2);
 }
 
+// Decode: n_q <= 8 new query rows (positions q_pos0 ..) of all G query heads
+// of one KV head against a long pre-rotated f16 K cache, the visited KV tiles
+// divided among n_splits workgroups per KV head (split-KV).  Row
+// rho = 32·wave + lane % 32 is head g = rho / n_q, position r = rho % n_q, so
+// one K/V tile read from HBM serves every head of the group.  Each workgroup
+// writes an fp32 partial (O, LSE) of its tiles; decode_combine_kernel merges
+// them by log-sum-exp.  Two LDS stages (64 KB) so that two workgroups share a
+// CU.  [CW §3 (the step's base applies to the new rows), §5.3 merge]
+template <int D, int NW, bool VT>
+__global__ __launch_bounds__(64 * NW) void attn_decode_kernel(const AttnParams p, const DecodeParams dp) {
+  using T = Tile<D, NW>;
+  __shared__ __attribute__((aligned(1024))) uint16_t k_st0[T::ELEMS], k_st1[T::ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_st0[T::ELEMS], v_st1[T::ELEMS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int h2 = lane >> 5;
+  const int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+  const int nq = (int)p.n_q;
+
+  const int rho = wave * 32 + l32;
+  const bool valid = rho < p.G * nq;
+  const int g = valid ? rho / nq : 0;
+  const int hq = hkv * p.G + g;
+  Rows32<D> rows;
+  rows.init_row(p, valid ? rho - g * nq : nq, p.q_pos0, p.q_pos0 + nq - 1);
+  f16x8 qf[D / 16];
+  load_q<D>(p, p.q + b * p.qs_b + hq * p.qs_h, rows.qi, h2, qf);
+
+  // this split's share of the tiles the rows visit
+  BlockTiles bt;
+  tile_range(p, p.q_pos0, p.q_pos0 + nq - 1, bt);
+  const int t_begin = (int)((int64_t)split * bt.ntl / dp.n_splits);
+  const int ntl = (int)((int64_t)(split + 1) * bt.ntl / dp.n_splits) - t_begin;
+  auto j0_of = [&](int t) { return bt.j0(t_begin + t); };
+
+  LdsCopy<D, NW, true> kcp;
+  LdsCopy<D, NW, false> vcp;
+  LdsCopyVT<D, NW> vtcp;
+  kcp.init(p.k + b * p.ks_b + hkv * p.ks_h, p.ks_s, p.n_kv, wave, lane);
+  if constexpr (VT)
+    vtcp.init(p.v + b * p.vs_b + hkv * p.vs_h, wave, lane);
+  else
+    vcp.init(p.v + b * p.vs_b + hkv * p.vs_h, p.vs_s, p.n_kv, wave, lane);
+  int koff[D / 16], voff[4];
+  operand_offsets<D, VT>(lane, koff, voff);
+
+  auto issue = [&](uint16_t* ks, uint16_t* vs, int t) {
+    const int j0 = j0_of(t);
+    kcp.issue(ks, j0);
+    if constexpr (VT)
+      vtcp.issue(vs, j0);
+    else
+      vcp.issue(vs, j0);
+  };
+  auto step = [&](const uint16_t* ks, const uint16_t* vs, uint16_t* ks_next, uint16_t* vs_next, int t) {
+    if (t + 1 < ntl) issue(ks_next, vs_next, t + 1);
+    f32x16 s_cur[2];
+    qk_tile<D>(ks, koff, qf, s_cur);
+    rows.mask(p, s_cur, j0_of(t), h2);
+    rows.rescale(rows.tile_max(p, s_cur));
+    bf16x8 pf[4];
+    rows.probs(p, s_cur, pf);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+        rows.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv_operand<D, VT>(vs, voff, db, kc), pf[kc],
+                                                                rows.oacc[db], 0, 0, 0);
+    stage_barrier<0>();
+  };
+  if (ntl > 0) issue(k_st0, v_st0, 0);
+  stage_barrier<0>();
+  for (int t = 0; t < ntl; t += 2) {
+    step(k_st0, v_st0, k_st1, v_st1, t);
+    if (t + 1 >= ntl) break;
+    step(k_st1, v_st1, k_st0, v_st0, t + 1);
+  }
+
+  // this split's partial, fp32 [B][Hq][n_q][d] and [B][Hq][n_q]
+  AttnParams pp = p;
+  const int64_t rows_all = (int64_t)p.B * p.Hq * nq;
+  pp.o = dp.o_part + split * rows_all * D;
+  pp.lse = dp.lse_part + split * rows_all;
+  pp.os_b = (int64_t)p.Hq * nq * D;
+  pp.os_h = (int64_t)nq * D;
+  pp.os_s = D;
+  pp.ls_b = (int64_t)p.Hq * nq;
+  pp.ls_h = nq;
+  pp.o_mode = 1;
+  rows.store(pp, b, hq, h2);
+}
+
 // Explicit instantiations: with only the implicit ones from launch_dn, the
 // host pass emitted the launch stub of the first k_mode of each head size
 // and left the others undefined (the library then fails to load).
@@ -707,6 +824,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
 LCX_ATTN_INST(64, kNWd64)
 LCX_ATTN_INST(128, kNWd128)
 #undef LCX_ATTN_INST
+template __global__ void attn_decode_kernel<64, 1, false>(const AttnParams, const DecodeParams);
+template __global__ void attn_decode_kernel<64, 2, false>(const AttnParams, const DecodeParams);
+template __global__ void attn_decode_kernel<64, 1, true>(const AttnParams, const DecodeParams);
+template __global__ void attn_decode_kernel<64, 2, true>(const AttnParams, const DecodeParams);
+template __global__ void attn_decode_kernel<128, 1, false>(const AttnParams, const DecodeParams);
+template __global__ void attn_decode_kernel<128, 2, false>(const AttnParams, const DecodeParams);
+template __global__ void attn_decode_kernel<128, 1, true>(const AttnParams, const DecodeParams);
+template __global__ void attn_decode_kernel<128, 2, true>(const AttnParams, const DecodeParams);
 
 template <int D, int NW, bool VT>
 hipError_t launch_dv(const AttnParams& p, hipStream_t s, unsigned grid) {
@@ -727,6 +852,21 @@ hipError_t launch_dn(const AttnParams& p, hipStream_t s, unsigned grid) {
 }  // namespace
 
 int attn_rows_per_block(int d) { return 32 * (d == 64 ? kNWd64 : kNWd128); }
+
+hipError_t launch_attn_decode(const AttnParams& p, const DecodeParams& dp, hipStream_t s) {
+  const int nw = p.G * (int)p.n_q > 32 ? 2 : 1;
+  const dim3 grid((unsigned)dp.n_splits, (unsigned)p.Hkv, (unsigned)p.B), block(64 * nw);
+#define LCX_DEC(D, NW, VT) hipLaunchKernelGGL((attn_decode_kernel<D, NW, VT>), grid, block, 0, s, p, dp)
+  if (p.d == 64) {
+    if (nw == 1) { if (p.v_tiled) LCX_DEC(64, 1, true); else LCX_DEC(64, 1, false); }
+    else { if (p.v_tiled) LCX_DEC(64, 2, true); else LCX_DEC(64, 2, false); }
+  } else {
+    if (nw == 1) { if (p.v_tiled) LCX_DEC(128, 1, true); else LCX_DEC(128, 1, false); }
+    else { if (p.v_tiled) LCX_DEC(128, 2, true); else LCX_DEC(128, 2, false); }
+  }
+#undef LCX_DEC
+  return hipGetLastError();
+}
 
 hipError_t launch_attn_fwd(const AttnParams& p_in, hipStream_t s) {
   AttnParams p = p_in;

@@ -161,3 +161,66 @@ hipError_t launch_finalize(const float* o_acc, const float* lse_acc, void* o, in
 }
 
 }  // namespace lcx
+
+// Combine of the split-KV decode partials: for each query row, the n_splits
+// (O_s, L_s) pairs (L_s = -inf: a split with no kept key) merge as
+// L = log sum_s e^(L_s), O = sum_s e^(L_s - L) O_s, accumulated with a
+// running maximum.  One workgroup of d/4 threads per row, 16 bytes each.
+namespace lcx {
+
+namespace {
+
+template <int D>
+__global__ __launch_bounds__(D / 4) void decode_combine_kernel(const AttnParams p, const DecodeParams dp) {
+  const int64_t row = blockIdx.x;  // (b·Hq + hq)·n_q + r
+  const int nq = (int)p.n_q;
+  const int r = (int)(row % nq);
+  const int64_t bh = row / nq;
+  const int hq = (int)(bh % p.Hq);
+  const int b = (int)(bh / p.Hq);
+  const int64_t rows_all = (int64_t)p.B * p.Hq * nq;
+  const int c = threadIdx.x;
+  float m = -INFINITY, l = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < dp.n_splits; ++sp) {
+    const float ls = dp.lse_part[sp * rows_all + row];
+    if (ls == -INFINITY) continue;
+    const f32x4 o = *reinterpret_cast<const f32x4*>(dp.o_part + (sp * rows_all + row) * D + 4 * c);
+    if (ls > m) {
+      const float sc = (m == -INFINITY) ? 0.f : expf(m - ls);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] *= sc;
+      l *= sc;
+      m = ls;
+    }
+    const float w = expf(ls - m);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += w * o[e];
+    l += w;
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (p.o_mode == 0) {
+    uint16_t* op = static_cast<uint16_t*>(p.o) + b * p.os_b + hq * p.os_h + r * p.os_s + 4 * c;
+    u32x2 w = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+    *reinterpret_cast<u32x2*>(op) = w;
+  } else {
+    float* op = static_cast<float*>(p.o) + b * p.os_b + hq * p.os_h + r * p.os_s + 4 * c;
+    f32x4 w = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    *reinterpret_cast<f32x4*>(op) = w;
+  }
+  if (c == 0) p.lse[b * p.ls_b + hq * p.ls_h + r] = l > 0.f ? m + logf(l) : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_decode_combine(const AttnParams& p, const DecodeParams& dp, hipStream_t s) {
+  const int64_t rows = (int64_t)p.B * p.Hq * p.n_q;
+  if (rows == 0) return hipSuccess;
+  if (p.d == 64)
+    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3((unsigned)rows), dim3(16), 0, s, p, dp);
+  else
+    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((unsigned)rows), dim3(32), 0, s, p, dp);
+  return hipGetLastError();
+}
+
+}  // namespace lcx

@@ -324,6 +324,28 @@ lcx_status lcx_attn_fwd(const lcx_attn_args* a, hipStream_t stream) {
   return hip_status(lcx::launch_attn_fwd(make_params(a), stream), "attention launch");
 }
 
+lcx_status lcx_attn_decode(const lcx_attn_args* a, int32_t n_splits, float* o_part, float* lse_part,
+                           hipStream_t stream) {
+  lcx_status st = check_attn(a, false);
+  if (st != LCX_OK) return st;
+  if (a->accumulate) return fail(LCX_ERR_INVALID_ARG, "accumulate must be 0 for decode");
+  if (a->n_q > 8) return fail(LCX_ERR_UNSUPPORTED, "decode takes at most 8 new rows (n_q = %lld)", (long long)a->n_q);
+  if ((int64_t)(a->Hq / a->Hkv) * a->n_q > 64)
+    return fail(LCX_ERR_UNSUPPORTED, "decode needs (Hq/Hkv)·n_q <= 64");
+  if (a->rope_k || a->k_dtype != LCX_F16)
+    return fail(LCX_ERR_UNSUPPORTED, "decode reads a pre-rotated f16 K cache (rope_k = 0, k_dtype F16)");
+  if (n_splits < 1 || n_splits > 65535) return fail(LCX_ERR_INVALID_ARG, "n_splits %d outside 1..65535", n_splits);
+  if (a->B > 65535 || a->Hkv > 65535) return fail(LCX_ERR_UNSUPPORTED, "B and Hkv must be <= 65535");
+  if (!o_part || !lse_part) return fail(LCX_ERR_INVALID_ARG, "o_part and lse_part are required");
+  if (!aligned16(o_part)) return fail(LCX_ERR_UNSUPPORTED, "o_part must be 16-byte aligned");
+  if (a->n_q == 0) return ok();
+  lcx::AttnParams p = make_params(a);
+  lcx::DecodeParams dp{o_part, lse_part, n_splits};
+  hipError_t e = lcx::launch_attn_decode(p, dp, stream);
+  if (e != hipSuccess) return hip_status(e, "decode launch");
+  return hip_status(lcx::launch_decode_combine(p, dp, stream), "combine launch");
+}
+
 lcx_status lcx_attn_pack_v(const void* v, void* v_tiles, int32_t B, int32_t Hkv, int64_t n,
                            int32_t d, const int64_t v_strides[3], hipStream_t stream) {
   if (!v || !v_tiles || !v_strides) return fail(LCX_ERR_INVALID_ARG, "v, v_tiles and v_strides are required");

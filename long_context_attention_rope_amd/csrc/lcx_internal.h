@@ -67,6 +67,13 @@ struct PackVParams {
   int64_t n, n_tiles;
 };
 
+// decode (split-KV): fp32 partials [n_splits][B][Hq][n_q][d] and [n_splits][B][Hq][n_q]
+struct DecodeParams {
+  float* o_part;
+  float* lse_part;
+  int32_t n_splits;
+};
+
 struct MergeParams {
   float* o_acc;
   float* lse_acc;
@@ -85,6 +92,9 @@ struct MergeParams {
 hipError_t launch_rope_table(const RopeTableParams& p, hipStream_t s);
 hipError_t launch_rope_apply(const RopeApplyParams* slots, int n_slots, hipStream_t s);
 hipError_t launch_attn_fwd(const AttnParams& p, hipStream_t s);
+hipError_t launch_attn_decode(const AttnParams& p, const DecodeParams& dp, hipStream_t s);
+// merge the decode partials into o (bf16 or f32, strides of p) and lse
+hipError_t launch_decode_combine(const AttnParams& p, const DecodeParams& dp, hipStream_t s);
 hipError_t launch_attn_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_pack_v(const PackVParams& p, hipStream_t s);
 // fill (o, lse) rows with the empty state (0, -inf); o fp32 contiguous per row

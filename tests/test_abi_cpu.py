@@ -29,8 +29,8 @@ def _declared():
 
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["lcx_rope_freqs", "lcx_rope_apply_qk", "lcx_attn_fwd",
-                                  "lcx_attn_pack_v", "lcx_attn_merge", "lcx_attn_fwd_chunked",
-                                  "lcx_status_string", "lcx_last_error"])
+                                  "lcx_attn_decode", "lcx_attn_pack_v", "lcx_attn_merge",
+                                  "lcx_attn_fwd_chunked", "lcx_status_string", "lcx_last_error"])
 
 
 def test_library_exports_every_declared_symbol(lcx):
@@ -174,6 +174,22 @@ def test_chunked_rejects(lcx):
     # tiled V: chunks must start on a 64-key tile
     a3 = _args(lcx, o_dtype=lcx.F32, v_tiled=1, v_strides=(ctypes.c_int64 * 3)(16384, 16384, 0))
     assert lcx._lib.lcx_attn_fwd_chunked(ctypes.byref(a3), 96, FAKE, FAKE, None, None, None) == 1
+
+
+def test_decode_rejects(lcx):
+    f = lcx._lib.lcx_attn_decode
+    ok = dict(n_q=4, k_dtype=lcx.F16)
+    a = _args(lcx, **ok)
+    assert f(ctypes.byref(a), 0, FAKE, FAKE, None) == 1           # n_splits
+    assert f(ctypes.byref(a), 8, None, FAKE, None) == 1           # workspace
+    assert f(ctypes.byref(_args(lcx, n_q=9, k_dtype=lcx.F16)), 8, FAKE, FAKE, None) == 2
+    assert f(ctypes.byref(_args(lcx, n_q=8, Hq=16, Hkv=1, q_strides=(ctypes.c_int64 * 3)(16 * 256 * 64, 256 * 64, 64),
+                                o_strides=(ctypes.c_int64 * 3)(16 * 256 * 64, 256 * 64, 64),
+                                lse_strides=(ctypes.c_int64 * 2)(16 * 256, 256), k_dtype=lcx.F16)),
+             8, FAKE, FAKE, None) == 2                            # (Hq/Hkv)·n_q > 64
+    assert f(ctypes.byref(_args(lcx, n_q=4)), 8, FAKE, FAKE, None) == 2          # bf16 K
+    assert f(ctypes.byref(_args(lcx, n_q=4, k_dtype=lcx.F16, o_dtype=lcx.F32, accumulate=1)),
+             8, FAKE, FAKE, None) == 1
 
 
 def test_pack_v_rejects(lcx):
