@@ -179,6 +179,77 @@ def bench_chunked(args, w):
     print(json.dumps(out), flush=True)
 
 
+def bench_decode(args, w):
+    """Split-KV decode on the layer's KV cache: N new rows (positions n-N .. n-1)
+    of all query heads against the n cached keys.  A step = the RoPE table rows
+    of the new positions (the base for the current length) + lcx_attn_decode.
+    HBM-bound: the cache (K pre-rotated f16, V tiles bf16) is read once per step."""
+    import numpy as np
+    import torch
+
+    import fixtures
+    import long_context_attention_rope_amd as lcx
+
+    n_q = args.decode
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q = to_dev(fixtures.normal_bf16(w.seed, fixtures.Q_ID, (w.B, w.Hq, n_q, w.d)))
+    k = to_dev(fixtures.normal_bf16(w.seed, fixtures.K_ID, (w.B, w.Hkv, w.n, w.d)))
+    v = to_dev(fixtures.normal_bf16(w.seed, fixtures.V_ID, (w.B, w.Hkv, w.n, w.d)))
+    cfg = lcx.rope_cfg(w.scheme, w.base, w.d, w.L_train, w.L_target, w.cur_len, w.alpha, w.beta)
+    # the cache: K rotated once (when it was written), V in tiles
+    cos_all, sin_all = lcx.rope_tables(cfg, w.n, device=dev)
+    _, k_rot = lcx.rope_apply_qk(None, k, cos_all, sin_all)
+    v_tiles = lcx.pack_v(v)
+    del k, v, cos_all, sin_all
+    q_pos0 = w.n - n_q
+    cos = torch.empty((n_q, w.d // 2), dtype=torch.float32, device=dev)
+    sin = torch.empty_like(cos)
+    n_splits = args.splits or max(1, min(-(-512 // (w.B * w.Hkv)), w.n // 256))
+    o = torch.empty((w.B, w.Hq, n_q, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.Hq, n_q), dtype=torch.float32, device=dev)
+    o_part = torch.empty((n_splits, w.B, w.Hq, n_q, w.d), dtype=torch.float32, device=dev)
+    lse_part = torch.empty((n_splits, w.B, w.Hq, n_q), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        lcx.rope_freqs(cfg, cos, sin, q_pos0)
+        lcx.attn_decode(q, k_rot, v_tiles, o, lse, n_splits=n_splits, o_part=o_part, lse_part=lse_part,
+                        rope_q=True, cos=cos, sin=sin, tab_pos0=q_pos0, rope=cfg, window=w.window,
+                        n_sink=w.n_sink, q_pos0=q_pos0)
+        if ev: ev[1].record(stream)
+
+    steps = max(args.steps, 50)
+    for _ in range(max(args.warmup, 5)):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    cache_bytes = w.B * w.Hkv * w.n * w.d * 2 + w.B * w.Hkv * 64 * ((w.n + 63) // 64) * w.d * 2
+    io_bytes = w.B * w.Hq * n_q * w.d * (2 + 2) + 2 * n_splits * w.B * w.Hq * n_q * (w.d + 1) * 4
+    gbs = (cache_bytes + io_bytes) / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "split-KV decode HBM GB/s (K f16 + V bf16 cache read once per step)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": max(args.warmup, 5),
+        "ms_per_step": round(ms, 4), "wall_ms_per_step": round(wall * 1e3 / steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name + "_decode", "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": w.d, "cached_keys": w.n, "new_rows": n_q, "splits_per_kv_head": n_splits,
+                   "rope": w.scheme, "v_layout": "tiles"},
+        "tokens_per_s": round(w.B * n_q / (ms * 1e-3), 1),
+        "roofline": {"kernel": "attn_decode + combine", "bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -191,6 +262,9 @@ def main():
                     help="V packed into 64-key tiles by lcx_attn_pack_v inside the step (default) or read as rows")
     ap.add_argument("--cpu-rows", type=int, default=None,
                     help="oracle rows for the CPU baseline (default 2048; 640 for the chunked workload; 0: skip)")
+    ap.add_argument("--decode", type=int, default=0, metavar="N",
+                    help="time split-KV decode of N new rows (1..8) against this layer's cache instead")
+    ap.add_argument("--splits", type=int, default=None, help="decode: workgroups per KV head")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-merge-check", dest="merge_check", action="store_false",
                     help="skip timing the merge pass on this layer's partial sizes")
@@ -221,6 +295,8 @@ def main():
         args.cpu_rows = 640 if w.chunk else 2048
     if w.chunk:
         return bench_chunked(args, w)
+    if args.decode:
+        return bench_decode(args, w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
