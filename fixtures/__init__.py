@@ -49,8 +49,8 @@ def _load():
     return _lib
 
 
-# tensor ids of the workload recipe
-Q_ID, K_ID, V_ID = 0, 1, 2
+# tensor ids of the workload recipe (DO: the upstream gradient dL/dO of the backward pass)
+Q_ID, K_ID, V_ID, DO_ID = 0, 1, 2, 3
 
 
 def normal_bf16(seed: int, tensor_id: int, shape, offset: int = 0) -> np.ndarray:

@@ -56,6 +56,9 @@ def _load():
             lib.oracle_attn_rows.argtypes = [vp, vp, vp, vp, i64, vp, vp, i32, i32, i32, i64, i64, i32,
                                              vp, f64, i32, f64, i32, i64, i32, vp, vp, vp]
             lib.oracle_attn_rows.restype = ctypes.c_int
+            lib.oracle_attn_bwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, i64, i64, vp,
+                                            f64, i32, f64, i32, i64, i32, vp, vp, vp, vp, vp]
+            lib.oracle_attn_bwd.restype = ctypes.c_int
             lib.oracle_merge.argtypes = [vp, vp, i64, i64, ctypes.c_int, vp, vp]
             lib.oracle_merge.restype = None
             _lib = lib
@@ -147,6 +150,51 @@ def attn_rows(q_rows, q_pos, q_head, q_batch, k, v, Hq: int, theta=None, pos_fac
     if rc != 0:
         raise ValueError("oracle_attn_rows: invalid arguments")
     return (o, lse, p) if want_p else (o, lse)
+
+
+def attn_bwd(q, k, v, dout, theta=None, pos_factor: float = 1.0, sm_scale: float | None = None,
+             causal: bool = True, window: int = -1, n_sink: int = 0, q_pos0: int = 0,
+             k_pos0: int = 0, row_sel=None, key_sel=None, want=("dq", "dk", "dv")):
+    """Gradients (dq, dk, dv) of the attention rows for dL/dO = dout.
+
+    q, dout [B][Hq][n_q][d] and k, v [B][Hkv][n_kv][d] are bf16 bits; theta None
+    means no rotation (gradients with respect to the given q, k), else the
+    gradients are with respect to the raw q, k.  row_sel [B][Hq][n_q] and
+    key_sel [B][Hkv][n_kv] (bool) restrict which dq rows / dk, dv keys are
+    computed; the rest are 0.  Outputs not in `want` are None.
+    """
+    lib = _load()
+    qq = _c(q, np.uint16)
+    kk = _c(k, np.uint16)
+    vv = _c(v, np.uint16)
+    go = _c(dout, np.uint16)
+    B, Hq, n_q, d = qq.shape
+    B2, Hkv, n_kv, d2 = kk.shape
+    assert B2 == B and d2 == d and vv.shape == kk.shape and go.shape == qq.shape
+    rope = theta is not None
+    th = _c(theta if rope else np.zeros(max(d // 2, 1)), np.float64)
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    rs = None if row_sel is None else _c(row_sel, np.uint8)
+    ks = None if key_sel is None else _c(key_sel, np.uint8)
+    if rs is not None:
+        assert rs.shape == (B, Hq, n_q)
+    if ks is not None:
+        assert ks.shape == (B, Hkv, n_kv)
+    dq = np.zeros(qq.shape, dtype=np.float64) if "dq" in want else None
+    dk = np.zeros(kk.shape, dtype=np.float64) if "dk" in want else None
+    dv = np.zeros(kk.shape, dtype=np.float64) if "dv" in want else None
+
+    def ptr(a):
+        return a.ctypes.data if a is not None else None
+
+    rc = lib.oracle_attn_bwd(qq.ctypes.data, kk.ctypes.data, vv.ctypes.data, go.ctypes.data, B, Hq,
+                             Hkv, n_q, n_kv, d, int(q_pos0), int(k_pos0), th.ctypes.data,
+                             float(pos_factor), int(rope), float(sm_scale), int(bool(causal)),
+                             int(window), int(n_sink), ptr(rs), ptr(ks), ptr(dq), ptr(dk), ptr(dv))
+    if rc != 0:
+        raise ValueError("oracle_attn_bwd: invalid arguments")
+    return dq, dk, dv
 
 
 def merge(lse_parts, o_parts):

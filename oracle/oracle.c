@@ -45,6 +45,14 @@
  *                       repeated K/V; full n x n brute force for n <= 64.
  *   oracle_merge      : any chunking of the keys, merged in any order,
  *                       equals the one-shot rows.
+ *   oracle_attn_bwd   : every element of dq, dk, dv against Richardson-
+ *                       extrapolated central differences of oracle_attn_rows
+ *                       on inputs whose perturbations are exact bf16 values
+ *                       (RoPE, YaRN temperature, GQA, offsets, window+sinks,
+ *                       empty rows); sum_j dv_j = sum of dO over non-empty
+ *                       rows; sum_j R(p_j) dk_j = 0; sum <q, dq> = sum <k, dk>;
+ *                       V = 0 gives dq = dk = 0; one-key rows; GQA = summed
+ *                       MHA with repeated K/V.
  */
 #include <math.h>
 #include <stdint.h>
@@ -355,6 +363,249 @@ int oracle_attn_rows(const uint16_t* q_rows, const int64_t* q_pos, const int32_t
   for (int64_t bh = 0; bh < nheads; ++bh) free(krot[bh]);
   free(krot);
   free(need);
+  return 0;
+}
+
+/* R(m)^T applied to one d-vector: each pair turns back by pos·factor·theta'_i,
+ *   (y_{2i}, y_{2i+1}) -> (y_{2i}c + y_{2i+1}s, -y_{2i}s + y_{2i+1}c).
+ * The transpose of the rotation above: the chain rule through x~ = R(m) x. */
+static void rotate_vec_t(const double* y, double* x, int d, int64_t pos, const double* theta,
+                         double pos_factor) {
+  double p = (double)pos * pos_factor;
+  for (int i = 0; i < d / 2; ++i) {
+    double phi = p * theta[i];
+    double c = cos(phi), s = sin(phi);
+    double y0 = y[2 * i], y1 = y[2 * i + 1];
+    x[2 * i] = y0 * c + y1 * s;
+    x[2 * i + 1] = -y0 * s + y1 * c;
+  }
+}
+
+/*
+ * Gradient of steps a4-a8 (the backward pass).
+ * READING: the pages use blockwise attention for training but never write its
+ * backward pass out; this is the exact gradient of the forward definition in
+ * oracle_attn_rows for a loss L with dL/dO = dO, by the chain rule:
+ *   dV_j    = sum_i P_ij dO_i
+ *   dP_ij   = <dO_i, v_j>,   D_i = sum_j P_ij dP_ij
+ *   dS_ij   = P_ij (dP_ij - D_i)                 (softmax Jacobian)
+ *   dq~_i   = sm_scale sum_j dS_ij k~_j,   dk~_j = sm_scale sum_i dS_ij q~_i
+ *   dq_i    = R(p_i)^T dq~_i,  dk_j = R(p_j)^T dk~_j   (rope = 0: dq = dq~, dk = dk~)
+ * i runs over the rows of every query head that reads KV head g (GQA), j over
+ * the keys kept for row i (same mask as the forward); an empty row adds nothing.
+ *
+ * q, dout : [B][Hq][n_q][d] bf16 bits (raw q when rope = 1); query row r is at
+ *           position q_pos0 + r
+ * k, v    : [B][Hkv][n_kv][d] bf16 bits; key j at position k_pos0 + j
+ * row_sel : optional [B][Hq][n_q] flags, the rows whose dq is computed
+ * key_sel : optional [B][Hkv][n_kv] flags, the keys whose dk, dv are computed
+ *           (NULL: all).  A row is visited when its dq is wanted or when it
+ *           keeps a selected key; unselected outputs are 0.
+ * dq      : optional fp64 [B][Hq][n_q][d]; dk, dv: optional fp64 [B][Hkv][n_kv][d]
+ * Returns 0, or -1 on bad arguments.
+ */
+int oracle_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
+                    int32_t B, int32_t Hq, int32_t Hkv, int64_t n_q, int64_t n_kv, int32_t d,
+                    int64_t q_pos0, int64_t k_pos0, const double* theta, double pos_factor,
+                    int32_t rope, double sm_scale, int32_t causal, int64_t window, int32_t n_sink,
+                    const uint8_t* row_sel, const uint8_t* key_sel, double* dq, double* dk,
+                    double* dv) {
+  if (d < 2 || (d & 1) || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || B <= 0 || n_q < 0 || n_kv < 0)
+    return -1;
+  const int G = Hq / Hkv;
+  const int64_t nheads = (int64_t)B * Hkv;
+  if (dq) memset(dq, 0, sizeof(double) * (size_t)(B * (int64_t)Hq * n_q * d));
+  if (dk) memset(dk, 0, sizeof(double) * (size_t)(nheads * n_kv * d));
+  if (dv) memset(dv, 0, sizeof(double) * (size_t)(nheads * n_kv * d));
+  const int want_keys = (dk != NULL || dv != NULL);
+
+  /* selected keys: a compact index per (batch, kv head), in key order */
+  int64_t* sel_start = (int64_t*)calloc((size_t)nheads + 1, sizeof(int64_t));
+  for (int64_t bh = 0; bh < nheads; ++bh) {
+    int64_t c = 0;
+    if (want_keys)
+      for (int64_t j = 0; j < n_kv; ++j) c += key_sel ? (key_sel[bh * n_kv + j] != 0) : 1;
+    sel_start[bh + 1] = sel_start[bh] + c;
+  }
+  const int64_t n_sel = sel_start[nheads];
+  int64_t* sel_key = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_sel > 0 ? n_sel : 1));
+  for (int64_t bh = 0; bh < nheads && want_keys; ++bh) {
+    int64_t c = sel_start[bh];
+    for (int64_t j = 0; j < n_kv; ++j)
+      if (!key_sel || key_sel[bh * n_kv + j]) sel_key[c++] = j;
+  }
+
+  /* which (batch, kv head) pairs are needed, and their rotated keys */
+  char* need = (char*)calloc((size_t)nheads, 1);
+  for (int64_t bh = 0; bh < nheads; ++bh) {
+    if (sel_start[bh + 1] > sel_start[bh]) need[bh] = 1;
+    if (dq)
+      for (int gq = 0; gq < G && !need[bh]; ++gq)
+        for (int64_t r = 0; r < n_q; ++r) {
+          int64_t row = ((bh / Hkv) * Hq + (bh % Hkv) * G + gq) * n_q + r;
+          if (!row_sel || row_sel[row]) {
+            need[bh] = 1;
+            break;
+          }
+        }
+  }
+  double** krot = (double**)calloc((size_t)nheads, sizeof(double*));
+  for (int64_t bh = 0; bh < nheads; ++bh) {
+    if (!need[bh]) continue;
+    krot[bh] = (double*)malloc((size_t)(n_kv > 0 ? n_kv : 1) * d * sizeof(double));
+    const uint16_t* kb = k + bh * n_kv * d;
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < n_kv; ++j) {
+      double* x = (double*)malloc(sizeof(double) * d);
+      for (int c = 0; c < d; ++c) x[c] = bf16_bits_to_f64(kb[j * d + c]);
+      if (rope)
+        rotate_vec(x, krot[bh] + j * d, d, k_pos0 + j, theta, pos_factor);
+      else
+        memcpy(krot[bh] + j * d, x, sizeof(double) * d);
+      free(x);
+    }
+  }
+
+  /* per-thread accumulators of dk~ and dv for the selected keys */
+  int nthr = 1;
+#ifdef _OPENMP
+  nthr = omp_get_max_threads();
+#endif
+  double* acc_k = (double*)calloc((size_t)nthr * (size_t)(n_sel > 0 ? n_sel : 1) * d, sizeof(double));
+  double* acc_v = (double*)calloc((size_t)nthr * (size_t)(n_sel > 0 ? n_sel : 1) * d, sizeof(double));
+  const int64_t n_rows = (int64_t)B * Hq * n_q;
+
+#pragma omp parallel
+  {
+    int tid = 0;
+#ifdef _OPENMP
+    tid = omp_get_thread_num();
+#endif
+    double* my_k = acc_k + (size_t)tid * (size_t)(n_sel > 0 ? n_sel : 1) * d;
+    double* my_v = acc_v + (size_t)tid * (size_t)(n_sel > 0 ? n_sel : 1) * d;
+    double* qv = (double*)malloc(sizeof(double) * d);
+    double* qr = (double*)malloc(sizeof(double) * d);
+    double* go = (double*)malloc(sizeof(double) * d);
+    double* gq = (double*)malloc(sizeof(double) * d);
+    double* sc = (double*)malloc(sizeof(double) * (n_kv > 0 ? n_kv : 1));
+    double* pr = (double*)malloc(sizeof(double) * (n_kv > 0 ? n_kv : 1));
+    double* ds = (double*)malloc(sizeof(double) * (n_kv > 0 ? n_kv : 1));
+    char* keep = (char*)malloc((size_t)(n_kv > 0 ? n_kv : 1));
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t row = 0; row < n_rows; ++row) {
+      const int64_t r = row % n_q;
+      const int64_t bhq = row / n_q;
+      const int h = (int)(bhq % Hq);
+      const int64_t b = bhq / Hq;
+      const int g = (int)(((int64_t)h * Hkv) / Hq);
+      const int64_t bh = b * Hkv + g;
+      const int64_t qpos = q_pos0 + r;
+      const int want_dq = dq != NULL && (!row_sel || row_sel[row]);
+      int sees_sel = 0;
+      for (int64_t c = sel_start[bh]; c < sel_start[bh + 1] && !sees_sel; ++c)
+        sees_sel = kept(qpos, k_pos0 + sel_key[c], causal, window, n_sink);
+      if (!want_dq && !sees_sel) continue;
+
+      const double* kr = krot[bh];
+      const uint16_t* vb = v + bh * n_kv * d;
+      for (int c = 0; c < d; ++c) {
+        qv[c] = bf16_bits_to_f64(q[row * d + c]);
+        go[c] = bf16_bits_to_f64(dout[row * d + c]);
+      }
+      if (rope)
+        rotate_vec(qv, qr, d, qpos, theta, pos_factor);
+      else
+        memcpy(qr, qv, sizeof(double) * d);
+
+      /* forward quantities of this row: scores, max, probabilities */
+      double mx = -INFINITY;
+      for (int64_t j = 0; j < n_kv; ++j) {
+        keep[j] = (char)kept(qpos, k_pos0 + j, causal, window, n_sink);
+        if (!keep[j]) continue;
+        double acc = 0.0;
+        for (int c = 0; c < d; ++c) acc += qr[c] * kr[j * d + c];
+        sc[j] = sm_scale * acc;
+        if (sc[j] > mx) mx = sc[j];
+      }
+      if (mx == -INFINITY) continue; /* empty row: no gradient */
+      double z = 0.0;
+      for (int64_t j = 0; j < n_kv; ++j)
+        if (keep[j]) z += exp(sc[j] - mx);
+      /* dP_ij, D_i, dS_ij */
+      double dsum = 0.0;
+      for (int64_t j = 0; j < n_kv; ++j) {
+        pr[j] = keep[j] ? exp(sc[j] - mx) / z : 0.0;
+        ds[j] = 0.0;
+        if (!keep[j]) continue;
+        const uint16_t* vj = vb + j * d;
+        double dp = 0.0;
+        for (int c = 0; c < d; ++c) dp += go[c] * bf16_bits_to_f64(vj[c]);
+        ds[j] = dp; /* dP for now */
+        dsum += pr[j] * dp;
+      }
+      for (int64_t j = 0; j < n_kv; ++j) ds[j] = keep[j] ? pr[j] * (ds[j] - dsum) : 0.0;
+
+      if (want_dq) {
+        for (int c = 0; c < d; ++c) gq[c] = 0.0;
+        for (int64_t j = 0; j < n_kv; ++j) {
+          if (!keep[j]) continue;
+          for (int c = 0; c < d; ++c) gq[c] += ds[j] * kr[j * d + c];
+        }
+        for (int c = 0; c < d; ++c) gq[c] *= sm_scale;
+        if (rope)
+          rotate_vec_t(gq, dq + row * d, d, qpos, theta, pos_factor);
+        else
+          memcpy(dq + row * d, gq, sizeof(double) * d);
+      }
+      for (int64_t c = sel_start[bh]; c < sel_start[bh + 1]; ++c) {
+        const int64_t j = sel_key[c];
+        if (!keep[j]) continue;
+        for (int e = 0; e < d; ++e) {
+          my_k[c * d + e] += sm_scale * ds[j] * qr[e];
+          my_v[c * d + e] += pr[j] * go[e];
+        }
+      }
+    }
+    free(qv);
+    free(qr);
+    free(go);
+    free(gq);
+    free(sc);
+    free(pr);
+    free(ds);
+    free(keep);
+  }
+
+  /* reduce the per-thread sums, then dk = R(p_j)^T dk~ */
+  for (int64_t bh = 0; bh < nheads && want_keys; ++bh) {
+    for (int64_t c = sel_start[bh]; c < sel_start[bh + 1]; ++c) {
+      const int64_t j = sel_key[c];
+      double* tk = (double*)malloc(sizeof(double) * d);
+      for (int e = 0; e < d; ++e) {
+        double sk = 0.0, sv = 0.0;
+        for (int t = 0; t < nthr; ++t) {
+          sk += acc_k[((size_t)t * (size_t)(n_sel > 0 ? n_sel : 1) + c) * d + e];
+          sv += acc_v[((size_t)t * (size_t)(n_sel > 0 ? n_sel : 1) + c) * d + e];
+        }
+        tk[e] = sk;
+        if (dv) dv[(bh * n_kv + j) * d + e] = sv;
+      }
+      if (dk) {
+        if (rope)
+          rotate_vec_t(tk, dk + (bh * n_kv + j) * d, d, k_pos0 + j, theta, pos_factor);
+        else
+          memcpy(dk + (bh * n_kv + j) * d, tk, sizeof(double) * d);
+      }
+      free(tk);
+    }
+  }
+  free(acc_k);
+  free(acc_v);
+  for (int64_t bh = 0; bh < nheads; ++bh) free(krot[bh]);
+  free(krot);
+  free(need);
+  free(sel_key);
+  free(sel_start);
   return 0;
 }
 
