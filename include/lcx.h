@@ -235,6 +235,62 @@ lcx_status lcx_attn_merge(float* o_acc, float* lse_acc, const float* o_part, con
 lcx_status lcx_attn_fwd_chunked(const lcx_attn_args* a, int64_t chunk, float* o_acc, float* lse_acc,
                                 float* o_part, float* lse_part, hipStream_t stream);
 
+/* Arguments of lcx_attn_bwd.  The forward quantities must be those of the
+ * lcx_attn_fwd call being differentiated (same scale, mask and positions). */
+typedef struct {
+  const void* q;    /* q~ = R(p) q: rotated queries, bf16 [B][Hq][n_q][d] */
+  const void* k;    /* k~ = R(p) k: rotated keys, bf16 [B][Hkv][n_kv][d] */
+  const void* v;    /* bf16 [B][Hkv][n_kv][d] rows (not the tile layout) */
+  const void* o;    /* forward output [B][Hq][n_q][d], o_dtype */
+  const float* lse; /* forward LSE fp32 [B][Hq][n_q] (natural log; -inf: row with no key) */
+  const void* d_o;  /* dL/dO, bf16 [B][Hq][n_q][d] */
+  int32_t o_dtype;  /* LCX_BF16 or LCX_F32 */
+  int32_t B, Hq, Hkv, d; /* Hq % Hkv == 0; d in {64, 128} */
+  int64_t n_q, n_kv;
+  int64_t q_strides[3], k_strides[3], v_strides[3], o_strides[3], do_strides[3]; /* elements */
+  int64_t lse_strides[2];  /* elements: batch, head (unit row stride) */
+  int64_t q_pos0, k_pos0;  /* absolute positions of row 0 / key 0 */
+  const lcx_rope_cfg* rope; /* optional: supplies the YaRN logit multiplier */
+  float softmax_scale;      /* 0: (1/sqrt(d))·logit_mult(rope), as in the forward */
+  int32_t causal;           /* must be 1 */
+  int64_t window;           /* -1: none (same mask rules as lcx_attn_fwd) */
+  int32_t n_sink;
+  int32_t unrotate;         /* 1: dq = R(p)^T dq~ and dk = R(p)^T dk~ (the gradients of the raw
+                               q, k) from the tables; 0: the gradients of q~ and k~ */
+  const float* cos_tab;     /* tables of lcx_rope_freqs; required with unrotate, covering */
+  const float* sin_tab;     /* the query and the key positions */
+  int64_t tab_pos0, tab_len;
+  void* dq;                 /* [B][Hq][n_q][d], grad_dtype, overwritten */
+  void* dk;                 /* [B][Hkv][n_kv][d], grad_dtype, overwritten (summed over the */
+  void* dv;                 /* query heads of each KV head) */
+  int32_t grad_dtype;       /* LCX_F32 or LCX_BF16 */
+  int64_t dq_strides[3], dk_strides[3], dv_strides[3]; /* elements */
+  float* workspace;         /* fp32 [B][Hq][n_q][2], contiguous, 16-byte aligned, caller-owned
+                               scratch (per-row LSE·log2 e and D = <dO, O>) */
+} lcx_attn_bwd_args;
+
+/*
+ * Backward pass of lcx_attn_fwd: the gradients dq, dk, dv of a loss with
+ * dL/dO = d_o, by the chain rule through the softmax and the rotation:
+ *   P = exp(S - LSE) (rebuilt per tile from the saved LSE, S = sigma·q~·k~^T
+ *   over kept keys), dV = P^T dO, dP = dO V^T, D = rowsum(dO ∘ O),
+ *   dS = P ∘ (dP - D), dq~ = sigma·dS·k~, dk~ = sigma·dS^T·q~, and with
+ *   unrotate dq = R(p)^T dq~, dk = R(p)^T dk~.
+ * [上下文擴充套件 FlashAttention 的分塊計算策略 (blockwise, no n x n matrix kept);
+ * 技術原理 (q~ = R(m)·W_q·x); AI 大模型窗口上下文进化史 §4; 上下文窗口扩展技术 §4.1,
+ * §4.2 (mask).  The pages give no backward pass: this is the exact gradient.]
+ * Products on bf16 MFMA (P and dS rounded to bf16), fp32 accumulation; the
+ * forward's f16 q~/k~ option does not apply (pass bf16 q~, k~).
+ * Pointers of the query side (q, o, lse, d_o, dq, workspace) may be NULL when
+ * n_q = 0, those of the key side (k, v, dk, dv) when n_kv = 0; with no rows
+ * dk = dv = 0, with no keys dq = 0.
+ * Errors: INVALID_ARG for NULL pointers, bad sizes, Hq % Hkv != 0, window <
+ * -1, n_sink < 0, bad dtypes, unrotate without tables covering the positions;
+ * UNSUPPORTED for d not 64/128, causal == 0, non-16-byte-aligned rows or
+ * pointers, a row stride of 2^24 elements or more.
+ */
+lcx_status lcx_attn_bwd(const lcx_attn_bwd_args* a, hipStream_t stream);
+
 /* Name of a status code (static string). */
 const char* lcx_status_string(lcx_status s);
 

@@ -49,6 +49,20 @@ class AttnArgs(ctypes.Structure):
                 ("lse", _vp), ("accumulate", _i32), ("v_tiled", _i32)]
 
 
+class BwdArgs(ctypes.Structure):
+    _fields_ = [("q", _vp), ("k", _vp), ("v", _vp), ("o", _vp), ("lse", _vp), ("d_o", _vp),
+                ("o_dtype", _i32), ("B", _i32), ("Hq", _i32), ("Hkv", _i32), ("d", _i32),
+                ("n_q", _i64), ("n_kv", _i64),
+                ("q_strides", _i64 * 3), ("k_strides", _i64 * 3), ("v_strides", _i64 * 3),
+                ("o_strides", _i64 * 3), ("do_strides", _i64 * 3), ("lse_strides", _i64 * 2),
+                ("q_pos0", _i64), ("k_pos0", _i64), ("rope", ctypes.POINTER(RopeCfg)),
+                ("softmax_scale", _f32), ("causal", _i32), ("window", _i64), ("n_sink", _i32),
+                ("unrotate", _i32), ("cos_tab", _vp), ("sin_tab", _vp), ("tab_pos0", _i64),
+                ("tab_len", _i64), ("dq", _vp), ("dk", _vp), ("dv", _vp), ("grad_dtype", _i32),
+                ("dq_strides", _i64 * 3), ("dk_strides", _i64 * 3), ("dv_strides", _i64 * 3),
+                ("workspace", _vp)]
+
+
 _P3 = ctypes.POINTER(_i64)
 _lib.lcx_status_string.argtypes = [ctypes.c_int]
 _lib.lcx_status_string.restype = ctypes.c_char_p
@@ -70,6 +84,8 @@ _lib.lcx_attn_pack_v.argtypes = [_vp, _vp, _i32, _i32, _i64, _i32, _P3, _vp]
 _lib.lcx_attn_decode.argtypes = [ctypes.POINTER(AttnArgs), _i32, _vp, _vp, _vp]
 _lib.lcx_attn_decode.restype = ctypes.c_int
 _lib.lcx_attn_pack_v.restype = ctypes.c_int
+_lib.lcx_attn_bwd.argtypes = [ctypes.POINTER(BwdArgs), _vp]
+_lib.lcx_attn_bwd.restype = ctypes.c_int
 
 
 class LcxError(RuntimeError):
@@ -276,3 +292,54 @@ def attn_merge(o_acc, lse_acc, o_part, lse_part, o_final=None):
                                _s3(o_acc), _s3(o_part), _s2(lse_acc), _s2(lse_part), _ptr(o_final),
                                fdt, _s3(o_final) if o_final is not None else None, _stream(o_acc)))
     return o_acc, lse_acc
+
+
+def attn_bwd(q, k, v, o, lse, dout, *, dq=None, dk=None, dv=None, workspace=None, unrotate=False,
+             cos=None, sin=None, tab_pos0=0, rope=None, softmax_scale=0.0, window=-1, n_sink=0,
+             q_pos0=0, k_pos0=0, grad_dtype=torch.float32, causal=True):
+    """lcx_attn_bwd.  q, k: the rotated bf16 q~ [B,Hq,n_q,d] and k~ [B,Hkv,n_kv,d] the
+    forward used; v bf16 rows; o, lse: the forward's outputs; dout = dL/dO bf16.  With
+    unrotate the gradients are those of the raw q, k (tables cos/sin required).
+    Returns (dq, dk, dv) in grad_dtype; workspace (fp32 [B,Hq,n_q,2]) is allocated when
+    not given."""
+    B, Hq, n_q, d = q.shape
+    Hkv, n_kv = k.shape[1], k.shape[2]
+    dev = q.device
+    if dq is None:
+        dq = torch.empty((B, Hq, n_q, d), dtype=grad_dtype, device=dev)
+    if dk is None:
+        dk = torch.empty((B, Hkv, n_kv, d), dtype=grad_dtype, device=dev)
+    if dv is None:
+        dv = torch.empty((B, Hkv, n_kv, d), dtype=grad_dtype, device=dev)
+    if workspace is None:
+        workspace = torch.empty((B, Hq, n_q, 2), dtype=torch.float32, device=dev)
+    if not workspace.is_contiguous() or tuple(workspace.shape) != (B, Hq, n_q, 2):
+        raise ValueError("workspace must be a contiguous fp32 [B, Hq, n_q, 2] tensor")
+    if not (dq.dtype == dk.dtype == dv.dtype):
+        raise ValueError("dq, dk, dv must share one dtype")
+    if lse.stride(2) != 1:
+        raise ValueError("lse rows must be contiguous")
+    a = BwdArgs()
+    a.q, a.k, a.v, a.o, a.lse, a.d_o = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                        lse.data_ptr(), dout.data_ptr())
+    a.o_dtype = _DT[o.dtype]
+    a.B, a.Hq, a.Hkv, a.d = B, Hq, Hkv, d
+    a.n_q, a.n_kv = n_q, n_kv
+    a.q_strides, a.k_strides, a.v_strides = _s3(q), _s3(k), _s3(v)
+    a.o_strides, a.do_strides, a.lse_strides = _s3(o), _s3(dout), _s2(lse)
+    a.q_pos0, a.k_pos0 = q_pos0, k_pos0
+    a.rope = ctypes.pointer(rope) if rope is not None else None
+    a.softmax_scale = softmax_scale
+    a.causal = int(causal)
+    a.window, a.n_sink = window, n_sink
+    a.unrotate = int(unrotate)
+    a.cos_tab = cos.data_ptr() if cos is not None else None
+    a.sin_tab = sin.data_ptr() if sin is not None else None
+    a.tab_pos0 = tab_pos0
+    a.tab_len = cos.shape[0] if cos is not None else 0
+    a.dq, a.dk, a.dv = dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    a.grad_dtype = _DT[dq.dtype]
+    a.dq_strides, a.dk_strides, a.dv_strides = _s3(dq), _s3(dk), _s3(dv)
+    a.workspace = workspace.data_ptr()
+    _check(_lib.lcx_attn_bwd(ctypes.byref(a), _stream(q)))
+    return dq, dk, dv

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 SO = os.path.join(HERE, "liblcx.so")
-SOURCES = ["lcx_api.hip", "rope.hip", "attn_fwd.hip", "attn_merge.hip", "pack_v.hip"]
+SOURCES = ["lcx_api.hip", "rope.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_merge.hip", "pack_v.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

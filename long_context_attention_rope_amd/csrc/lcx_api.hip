@@ -213,6 +213,99 @@ lcx::AttnParams make_params(const lcx_attn_args* a) {
   return p;
 }
 
+lcx_status check_bwd(const lcx_attn_bwd_args* a) {
+  if (!a) return fail(LCX_ERR_INVALID_ARG, "args is NULL");
+  if (a->B < 1 || a->Hq < 1 || a->Hkv < 1) return fail(LCX_ERR_INVALID_ARG, "B, Hq, Hkv must be >= 1");
+  if (a->n_q > 0 && (!a->q || !a->o || !a->lse || !a->d_o || !a->dq || !a->workspace))
+    return fail(LCX_ERR_INVALID_ARG, "q, o, lse, d_o, dq and workspace are required when n_q > 0");
+  if (a->n_kv > 0 && (!a->k || !a->v || !a->dk || !a->dv))
+    return fail(LCX_ERR_INVALID_ARG, "k, v, dk and dv are required when n_kv > 0");
+  if (a->Hq % a->Hkv) return fail(LCX_ERR_INVALID_ARG, "Hq %d is not a multiple of Hkv %d", a->Hq, a->Hkv);
+  if (a->n_q < 0 || a->n_kv < 0) return fail(LCX_ERR_INVALID_ARG, "n_q and n_kv must be >= 0");
+  if (a->d != 64 && a->d != 128) return fail(LCX_ERR_UNSUPPORTED, "head dim %d (kernels: 64, 128)", a->d);
+  if (a->causal != 1) return fail(LCX_ERR_UNSUPPORTED, "only causal attention is implemented");
+  if (a->window < -1) return fail(LCX_ERR_INVALID_ARG, "window %lld < -1", (long long)a->window);
+  if (a->n_sink < 0) return fail(LCX_ERR_INVALID_ARG, "n_sink %d < 0", a->n_sink);
+  if (a->o_dtype != LCX_BF16 && a->o_dtype != LCX_F32) return fail(LCX_ERR_INVALID_ARG, "o dtype");
+  if (a->grad_dtype != LCX_BF16 && a->grad_dtype != LCX_F32) return fail(LCX_ERR_INVALID_ARG, "grad dtype");
+  if (a->unrotate != 0 && a->unrotate != 1) return fail(LCX_ERR_INVALID_ARG, "unrotate must be 0 or 1");
+  if (!(a->softmax_scale >= 0.f) || !std::isfinite(a->softmax_scale))
+    return fail(LCX_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0 (0: default)");
+  if (a->rope) {
+    lcx_status st = check_cfg(a->rope);
+    if (st != LCX_OK) return st;
+  }
+  if (a->unrotate) {
+    if (!a->cos_tab || !a->sin_tab) return fail(LCX_ERR_INVALID_ARG, "unrotate needs the RoPE tables");
+    if (!covers(a->tab_pos0, a->tab_len, a->q_pos0, a->n_q) || !covers(a->tab_pos0, a->tab_len, a->k_pos0, a->n_kv))
+      return fail(LCX_ERR_INVALID_ARG, "table rows do not cover the query and key positions");
+    if (!aligned16(a->cos_tab) || !aligned16(a->sin_tab))
+      return fail(LCX_ERR_UNSUPPORTED, "tables must be 16-byte aligned");
+  }
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o) || !aligned16(a->d_o) ||
+      !aligned16(a->dq) || !aligned16(a->dk) || !aligned16(a->dv) || !aligned16(a->workspace))
+    return fail(LCX_ERR_UNSUPPORTED, "tensors and workspace must be 16-byte aligned");
+  if (!strides_ok(a->q_strides, 8) || !strides_ok(a->k_strides, 8) || !strides_ok(a->v_strides, 8) ||
+      !strides_ok(a->do_strides, 8))
+    return fail(LCX_ERR_UNSUPPORTED, "q/k/v/d_o strides must be non-negative multiples of 8 elements");
+  if (!strides_ok(a->o_strides, a->o_dtype == LCX_F32 ? 4 : 8))
+    return fail(LCX_ERR_UNSUPPORTED, "o strides must keep rows 16-byte aligned");
+  if (!strides_ok(a->dq_strides, 4) || !strides_ok(a->dk_strides, 4) || !strides_ok(a->dv_strides, 4))
+    return fail(LCX_ERR_UNSUPPORTED, "gradient strides must be non-negative multiples of 4 elements");
+  if (a->lse_strides[0] < 0 || a->lse_strides[1] < 0)
+    return fail(LCX_ERR_INVALID_ARG, "lse strides must be >= 0");
+  // one 64-row tile is addressed with 32-bit buffer offsets
+  const int64_t lim = (int64_t)1 << 24;
+  if (a->q_strides[2] >= lim || a->k_strides[2] >= lim || a->v_strides[2] >= lim || a->do_strides[2] >= lim)
+    return fail(LCX_ERR_UNSUPPORTED, "row strides must be below 2^24 elements");
+  const int64_t bm = lcx::attn_bwd_rows_per_block(a->d), bk = lcx::attn_bwd_keys_per_block(a->d);
+  if ((int64_t)a->B * a->Hq * ((a->n_q + bm - 1) / bm) >= (int64_t)1 << 31 ||
+      (int64_t)a->B * a->Hkv * ((a->n_kv + bk - 1) / bk) >= (int64_t)1 << 31 ||
+      (a->n_q + 63) / 64 * (a->Hq / a->Hkv) >= (int64_t)1 << 31)
+    return fail(LCX_ERR_UNSUPPORTED, "problem too large for one launch");
+  return LCX_OK;
+}
+
+lcx::BwdParams make_bwd_params(const lcx_attn_bwd_args* a) {
+  lcx::BwdParams p{};
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.k = static_cast<const uint16_t*>(a->k);
+  p.v = static_cast<const uint16_t*>(a->v);
+  p.o = a->o;
+  p.lse = a->lse;
+  p.dout = static_cast<const uint16_t*>(a->d_o);
+  p.stats = a->workspace;
+  p.dq = a->dq; p.dk = a->dk; p.dv = a->dv;
+  p.cos_tab = a->cos_tab; p.sin_tab = a->sin_tab;
+  p.qs_b = a->q_strides[0]; p.qs_h = a->q_strides[1]; p.qs_s = a->q_strides[2];
+  p.ks_b = a->k_strides[0]; p.ks_h = a->k_strides[1]; p.ks_s = a->k_strides[2];
+  p.vs_b = a->v_strides[0]; p.vs_h = a->v_strides[1]; p.vs_s = a->v_strides[2];
+  p.os_b = a->o_strides[0]; p.os_h = a->o_strides[1]; p.os_s = a->o_strides[2];
+  p.dos_b = a->do_strides[0]; p.dos_h = a->do_strides[1]; p.dos_s = a->do_strides[2];
+  p.ls_b = a->lse_strides[0]; p.ls_h = a->lse_strides[1];
+  p.dqs_b = a->dq_strides[0]; p.dqs_h = a->dq_strides[1]; p.dqs_s = a->dq_strides[2];
+  p.dks_b = a->dk_strides[0]; p.dks_h = a->dk_strides[1]; p.dks_s = a->dk_strides[2];
+  p.dvs_b = a->dv_strides[0]; p.dvs_h = a->dv_strides[1]; p.dvs_s = a->dv_strides[2];
+  p.n_q = a->n_q; p.n_kv = a->n_kv; p.q_pos0 = a->q_pos0; p.k_pos0 = a->k_pos0;
+  p.tab_pos0 = a->tab_pos0;
+  p.window = a->window;
+  double mult = 1.0;
+  if (a->rope) {
+    double th[2 * lcx::kMaxHalfDim], pf;
+    if (a->rope->head_dim <= 4 * lcx::kMaxHalfDim) scheme_freqs(*a->rope, th, &pf, &mult);
+  }
+  const double sigma = a->softmax_scale > 0.f ? (double)a->softmax_scale : mult / std::sqrt((double)a->d);
+  p.scale = (float)sigma;
+  p.scale_log2 = (float)(sigma * 1.4426950408889634074);
+  p.B = a->B; p.Hq = a->Hq; p.Hkv = a->Hkv; p.G = a->Hq / a->Hkv; p.d = a->d;
+  p.n_sink = a->n_sink;
+  p.causal = a->causal;
+  p.o_f32 = a->o_dtype == LCX_F32;
+  p.grad_f32 = a->grad_dtype == LCX_F32;
+  p.unrotate = a->unrotate;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -469,6 +562,12 @@ lcx_status lcx_attn_fwd_chunked(const lcx_attn_args* a, int64_t chunk, float* o_
     if (e != hipSuccess) return hip_status(e, "finalize launch");
   }
   return ok();
+}
+
+lcx_status lcx_attn_bwd(const lcx_attn_bwd_args* a, hipStream_t stream) {
+  lcx_status st = check_bwd(a);
+  if (st != LCX_OK) return st;
+  return hip_status(lcx::launch_attn_bwd(make_bwd_params(a), stream), "backward launch");
 }
 
 }  // extern "C"

@@ -59,6 +59,43 @@ struct AttnParams {
   int32_t v_tiled;  // 1: v in the 64-key tile layout (vs_b, vs_h its strides)
 };
 
+// backward pass (gradients of the attention rows)
+struct BwdParams {
+  const uint16_t* q;   // q~ bf16 [B][Hq][n_q][d]
+  const uint16_t* k;   // k~ bf16 [B][Hkv][n_kv][d]
+  const uint16_t* v;   // bf16 rows
+  const void* o;       // forward output, bf16 or f32
+  const float* lse;    // forward LSE
+  const uint16_t* dout;  // dL/dO bf16
+  float* stats;        // workspace fp32 [B][Hq][n_q][2]: (LSE·log2 e, D)
+  void* dq;
+  void* dk;
+  void* dv;
+  const float* cos_tab;
+  const float* sin_tab;
+  int64_t qs_b, qs_h, qs_s;
+  int64_t ks_b, ks_h, ks_s;
+  int64_t vs_b, vs_h, vs_s;
+  int64_t os_b, os_h, os_s;
+  int64_t dos_b, dos_h, dos_s;
+  int64_t ls_b, ls_h;
+  int64_t dqs_b, dqs_h, dqs_s;
+  int64_t dks_b, dks_h, dks_s;
+  int64_t dvs_b, dvs_h, dvs_s;
+  int64_t n_q, n_kv, q_pos0, k_pos0, tab_pos0;
+  int64_t window;
+  float scale;       // softmax scale sigma
+  float scale_log2;  // sigma·log2(e)
+  int32_t B, Hq, Hkv, G, d;
+  int32_t n_qblk;
+  int32_t n_sink;
+  int32_t causal;
+  int32_t xcd_map;
+  int32_t o_f32;     // forward output in fp32 (else bf16)
+  int32_t grad_f32;  // dq, dk, dv in fp32 (else bf16)
+  int32_t unrotate;  // 1: dq, dk turned back by R(p)^T from the tables
+};
+
 struct PackVParams {
   const uint16_t* v;
   uint16_t* vt;
@@ -97,6 +134,10 @@ hipError_t launch_attn_decode(const AttnParams& p, const DecodeParams& dp, hipSt
 hipError_t launch_decode_combine(const AttnParams& p, const DecodeParams& dp, hipStream_t s);
 hipError_t launch_attn_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_pack_v(const PackVParams& p, hipStream_t s);
+// backward: row statistics, then the dq and the dk/dv kernels
+hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t s);
+int attn_bwd_rows_per_block(int d);  // dq kernel query rows per workgroup
+int attn_bwd_keys_per_block(int d);  // dk/dv kernel keys per workgroup
 // fill (o, lse) rows with the empty state (0, -inf); o fp32 contiguous per row
 hipError_t launch_fill_empty(float* o, float* lse, int32_t B, int32_t H, int64_t rows, int32_t d,
                              int64_t os_b, int64_t os_h, int64_t os_s, int64_t ls_b, int64_t ls_h,

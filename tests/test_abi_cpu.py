@@ -29,7 +29,7 @@ def _declared():
 
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["lcx_rope_freqs", "lcx_rope_apply_qk", "lcx_attn_fwd",
-                                  "lcx_attn_decode", "lcx_attn_pack_v", "lcx_attn_merge",
+                                  "lcx_attn_decode", "lcx_attn_pack_v", "lcx_attn_merge", "lcx_attn_bwd",
                                   "lcx_attn_fwd_chunked", "lcx_status_string", "lcx_last_error"])
 
 
@@ -190,6 +190,47 @@ def test_decode_rejects(lcx):
     assert f(ctypes.byref(_args(lcx, n_q=4)), 8, FAKE, FAKE, None) == 2          # bf16 K
     assert f(ctypes.byref(_args(lcx, n_q=4, k_dtype=lcx.F16, o_dtype=lcx.F32, accumulate=1)),
              8, FAKE, FAKE, None) == 1
+
+
+def _bwd_args(lcx, **kw):
+    a = lcx.BwdArgs()
+    a.q = a.k = a.v = a.o = a.lse = a.d_o = a.dq = a.dk = a.dv = a.workspace = FAKE
+    a.o_dtype = lcx.BF16
+    a.B, a.Hq, a.Hkv, a.d = 1, 4, 1, 64
+    a.n_q = a.n_kv = 256
+    qs = (ctypes.c_int64 * 3)(4 * 256 * 64, 256 * 64, 64)
+    ks = (ctypes.c_int64 * 3)(256 * 64, 256 * 64, 64)
+    a.q_strides = a.o_strides = a.do_strides = a.dq_strides = qs
+    a.k_strides = a.v_strides = a.dk_strides = a.dv_strides = ks
+    a.lse_strides = (ctypes.c_int64 * 2)(4 * 256, 256)
+    a.causal = 1
+    a.window = -1
+    a.grad_dtype = lcx.F32
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+BWD_BAD = [
+    (1, dict(d_o=None)), (1, dict(workspace=None)), (1, dict(dk=None)), (1, dict(Hq=6, Hkv=4)),
+    (1, dict(n_kv=-1)), (2, dict(d=96)), (2, dict(causal=0)), (1, dict(window=-2)), (1, dict(n_sink=-1)),
+    (1, dict(o_dtype=2)), (1, dict(grad_dtype=2)), (1, dict(unrotate=2)), (1, dict(unrotate=1)),
+    (1, dict(unrotate=1, cos_tab=FAKE, sin_tab=FAKE, tab_len=255)),
+    (1, dict(unrotate=1, cos_tab=FAKE, sin_tab=FAKE, tab_len=256, k_pos0=1)),
+    (1, dict(softmax_scale=float("nan"))), (2, dict(workspace=FAKE + 8)), (2, dict(dv=FAKE + 4)),
+    (2, dict(do_strides=(ctypes.c_int64 * 3)(0, 0, 60))), (2, dict(dk_strides=(ctypes.c_int64 * 3)(0, 0, 66))),
+    (2, dict(k_strides=(ctypes.c_int64 * 3)(0, 0, 1 << 24))),
+]
+
+
+@pytest.mark.parametrize("status,kw", BWD_BAD)
+def test_attn_bwd_rejects_before_launch(lcx, status, kw):
+    a = _bwd_args(lcx, **kw)
+    assert lcx._lib.lcx_attn_bwd(ctypes.byref(a), None) == status, lcx._lib.lcx_last_error()
+
+
+def test_attn_bwd_null_args(lcx):
+    assert lcx._lib.lcx_attn_bwd(None, None) == 1
 
 
 def test_pack_v_rejects(lcx):
