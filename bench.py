@@ -250,6 +250,105 @@ def bench_decode(args, w):
     print(json.dumps(out), flush=True)
 
 
+def cpu_baseline_bwd(w, m: int):
+    """The oracle's backward pass (dq, dk, dv, every element) on the first m
+    positions of every head of the layer: a causal prefix of the same shape."""
+    import numpy as np
+    import fixtures
+    import oracle
+    th, pf, lm = oracle.rope_freqs(w.scheme, w.base, w.d, w.L_train, w.L_target, w.cur_len,
+                                   w.alpha, w.beta)
+    def prefix(tid, H):
+        # rows 0..m-1 of every (batch, head) of a [B, H, n, d] tensor
+        flat = (np.arange(w.B * H, dtype=np.int64)[:, None] * w.n + np.arange(m)[None, :]).reshape(-1)
+        return fixtures.rows_bf16(w.seed, tid, flat, w.d).reshape(w.B, H, m, w.d)
+    q, g = prefix(fixtures.Q_ID, w.Hq), prefix(fixtures.DO_ID, w.Hq)
+    k, v = prefix(fixtures.K_ID, w.Hkv), prefix(fixtures.V_ID, w.Hkv)
+    t0 = time.perf_counter()
+    oracle.attn_bwd(q, k, v, g, th, pf, lm / np.sqrt(w.d), True, w.window, w.n_sink)
+    dt = time.perf_counter() - t0
+    flop = 2.5 * w.with_(n=m).flop()
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"the first {m} positions of all {w.Hq} query heads of the same layer (dq, dk, dv "
+                      f"in full), fp64, {flop:.3e} algorithmic FLOP (5 products per kept pair)"}
+
+
+def bench_backward(args, w):
+    """The backward pass of the layer: a step = lcx_attn_bwd (row statistics,
+    dq kernel, dk/dv kernel) with its inputs resident in HBM: q~ and k~ rotated
+    to bf16, V rows, the forward's O (bf16) and LSE, a synthetic dL/dO; the
+    gradients of the raw q, k (inverse rotation in the epilogues) in fp32."""
+    import numpy as np
+    import torch
+
+    import fixtures
+    import long_context_attention_rope_amd as lcx
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q = to_dev(fixtures.normal_bf16(w.seed, fixtures.Q_ID, (w.B, w.Hq, w.n, w.d)))
+    k = to_dev(fixtures.normal_bf16(w.seed, fixtures.K_ID, (w.B, w.Hkv, w.n, w.d)))
+    v = to_dev(fixtures.normal_bf16(w.seed, fixtures.V_ID, (w.B, w.Hkv, w.n, w.d)))
+    g = to_dev(fixtures.normal_bf16(w.seed, fixtures.DO_ID, (w.B, w.Hq, w.n, w.d)))
+    cfg = lcx.rope_cfg(w.scheme, w.base, w.d, w.L_train, w.L_target, w.cur_len, w.alpha, w.beta)
+    cos, sin = lcx.rope_tables(cfg, w.n, device=dev)
+    _, kf = lcx.rope_apply_qk(None, k, cos, sin)
+    o, lse = lcx.attn_fwd(q, kf, lcx.pack_v(v), rope_q=True, cos=cos, sin=sin, rope=cfg,
+                          window=w.window, n_sink=w.n_sink)
+    del kf
+    qr, kr = lcx.rope_apply_qk(q, k, cos, sin, out_dtype=torch.bfloat16)
+    del q, k
+    dq = torch.empty((w.B, w.Hq, w.n, w.d), dtype=torch.float32, device=dev)
+    dk = torch.empty((w.B, w.Hkv, w.n, w.d), dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+    ws = torch.empty((w.B, w.Hq, w.n, 2), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        lcx.attn_bwd(qr, kr, v, o, lse, g, dq=dq, dk=dk, dv=dv, workspace=ws, unrotate=True, cos=cos,
+                     sin=sin, rope=cfg, window=w.window, n_sink=w.n_sink)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    bwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ms_step = wall * 1e3 / args.steps
+    flop = 2.5 * w.flop()   # S, dP, dV, dK, dQ: five products per kept pair
+    value = flop / (ms_step * 1e-3) / 1e12
+    ach = flop / (bwd_ms * 1e-3) / 1e12
+    out = {
+        "metric": "causal attn backward TFLOP/s (5 products per kept pair) + % bf16 MFMA peak, "
+                  "70B-shape GQA layer at 128K ctx",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name + "_backward", "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": w.d, "seq_len": w.n, "rope": w.scheme, "causal": True,
+                   "window": w.window, "n_sink": w.n_sink, "grads": "dq, dk, dv fp32 (raw q, k)",
+                   "mfma": "bf16 operands (q~, k~, V, dO, P, dS), fp32 accumulate",
+                   "executed_products_per_pair": 7},
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "tokens_per_s": round(w.B * w.n / (ms_step * 1e-3), 1),
+        "kernels_ms": {"attn_bwd (stats + dq + dk/dv)": round(bwd_ms, 3)},
+        "roofline": {"kernel": "attn_bwd (stats + dq + dk/dv launches)", "bound": "mfma",
+                     "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+    if args.cpu_rows > 0:
+        out["cpu_baseline"] = cpu_baseline_bwd(w, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -265,6 +364,9 @@ def main():
     ap.add_argument("--decode", type=int, default=0, metavar="N",
                     help="time split-KV decode of N new rows (1..8) against this layer's cache instead")
     ap.add_argument("--splits", type=int, default=None, help="decode: workgroups per KV head")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the backward pass (lcx_attn_bwd) of this layer instead; --cpu-rows is then "
+                         "the length of the prefix the oracle differentiates (default 2560)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-merge-check", dest="merge_check", action="store_false",
                     help="skip timing the merge pass on this layer's partial sizes")
@@ -292,7 +394,9 @@ def main():
     if args.warmup is None:
         args.warmup = 1 if w.chunk else 3
     if args.cpu_rows is None:
-        args.cpu_rows = 640 if w.chunk else 2048
+        args.cpu_rows = 640 if w.chunk else (2560 if args.bwd else 2048)
+    if args.bwd:
+        return bench_backward(args, w)
     if w.chunk:
         return bench_chunked(args, w)
     if args.decode:

@@ -26,9 +26,18 @@ FLAGS = [
 ]
 
 
+# per-source code generation options
+SOURCE_FLAGS = {
+    # MFMA results in VGPRs where the register budget allows: the backward's
+    # score accumulators feed VALU work, and AGPR results would each need a
+    # v_accvgpr_read first
+    "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

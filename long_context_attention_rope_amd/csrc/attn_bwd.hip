@@ -70,27 +70,26 @@ struct TileCopy {
   int64_t rs;
   int64_t n;
   int row0;
-  uint32_t off[LPW];
+  int lane;
 
-  __device__ __forceinline__ void init(int64_t stride, int64_t n_rows, int wave, int lane) {
+  __device__ __forceinline__ void init(int64_t stride, int64_t n_rows, int wave, int lane_) {
     rs = stride;
     n = n_rows;
     row0 = wave * LPW * RPL;
-#pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int r = row0 + i * RPL + lane / CPR;
-      const int c = (lane % CPR) ^ b_swz<D>(r);
-      off[i] = (uint32_t)(r * rs * 2) + (uint32_t)c * 16u;
-    }
+    lane = lane_;
   }
+  // the lane offsets are recomputed per copy (a few VALU ops) rather than
+  // held in registers across the step
   __device__ __forceinline__ void issue(uint16_t* lds, const uint16_t* base, int64_t j0) const {
     const int64_t left = n - j0;
     const uint32_t rows = left <= 0 ? 0u : (left >= BN ? (uint32_t)BN : (uint32_t)left);
     const __amdgpu_buffer_rsrc_t r = make_rsrc(base + j0 * rs, rows * (uint32_t)(rs * 2));
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
+      const int row = row0 + i * RPL + lane / CPR;
+      const uint32_t off = (uint32_t)(row * rs * 2) + (uint32_t)(((lane % CPR) ^ b_swz<D>(row)) * 16);
       const uint32_t la = (uint32_t)(uintptr_t)(lds_void*)(lds + (row0 + i * RPL) * D);
-      lds_copy16(r, off[i], __builtin_amdgcn_readfirstlane(la));
+      lds_copy16(r, off, __builtin_amdgcn_readfirstlane(la));
     }
   }
 };
@@ -484,11 +483,63 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
   };
   constexpr int kLoads = 2 * C::LPW + 1;
 
+  // per-half registers of the step pipeline
+  struct HalfOps { bf16x8 q[D / 16], g[D / 16]; };          // row operands (A of S, dP)
+  struct HalfAcc { f32x16 s, dp; };                          // S, dP accumulators
+  struct HalfTr { bf16x8 g[D / 32][2], q[D / 32][2]; };      // transposed operands (A of dV, dK)
+  struct HalfSt { f32x4 a[4], c[4]; };                       // (LSE·log2 e, D) of the half's rows
+  struct HalfB { bf16x8 p[2], ds[2]; };                      // B operands of dV, dK
+
   auto step = [&](const uint16_t* qs, const uint16_t* gs, const float* ss, uint16_t* qs_n, uint16_t* gs_n,
                   float* ss_n, int s) {
     const bool pre = s + 2 < nsteps;
     if (pre) issue(qs_n, gs_n, ss_n, s + 2);
     const int64_t j0 = step_rows(s);
+    auto load_rows = [&](HalfOps& a, int rb) {
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        a.q[c] = to.row_op(qs, rb, c);
+        a.g[c] = to.row_op(gs, rb, c);
+      }
+    };
+    auto mfma_sdp = [&](const HalfOps& a, HalfAcc& c) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        c.s[r] = 0.f;
+        c.dp[r] = 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < D / 16; ++k) {
+        c.s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.q[k], kf[k], c.s, 0, 0, 0);
+        c.dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.g[k], vf[k], c.dp, 0, 0, 0);
+      }
+    };
+    auto load_tr = [&](HalfTr& t, int rb) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          t.g[db][k2] = to.tr_op(gs, db, 2 * rb + k2);
+          t.q[db][k2] = to.tr_op(qs, db, 2 * rb + k2);
+        }
+    };
+    auto load_stats = [&](HalfSt& t, int rb) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int row = rb * 32 + r4 * 8 + h * 4;
+        t.a[r4] = *reinterpret_cast<const f32x4*>(ss + SC::stat_off(row));
+        t.c[r4] = *reinterpret_cast<const f32x4*>(ss + SC::stat_off(row) + 4);
+      }
+    };
+    auto mfma_grad = [&](const HalfTr& t, const HalfB& b) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t.g[db][k2], b.p[k2], dvacc[db], 0, 0, 0);
+          dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t.q[db][k2], b.ds[k2], dkacc[db], 0, 0, 0);
+        }
+    };
     // mask facts of this tile: element (rb, r) is row 32rb + (r/4)·8 + 4h + r%4
     // of the tile and the lane's key
     const int64_t qpos_t = p.q_pos0 + j0;
@@ -498,55 +549,52 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
     const int hi = clamp_i32(qpos_t - kpos);  // causal: row off kept iff hi + off >= 0
     const int lo = p.window >= 0 ? clamp_i32(qpos_t - kpos - p.window) : -(1 << 30);  // lo + off <= 0
     const int rrem = clamp_tile(p.n_q - j0);
-    // two halves of 32 rows each: S, dP, then dV, dK over those rows
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      f32x16 sc, dp;
+    // mask of a tile that straddles an edge: -inf scores
+    auto mask = [&](HalfAcc& c, int rb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        sc[r] = 0.f;
-        dp[r] = 0.f;
+        const int off = rb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+        const bool ok = kvalid & (off < rrem) & (!p.causal | (hi + off >= 0)) & ((lo + off <= 0) | k_sink);
+        c.s[r] = ok ? c.s[r] : -INFINITY;
       }
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(to.row_op(qs, rb, c), kf[c], sc, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(to.row_op(gs, rb, c), vf[c], dp, 0, 0, 0);
-      }
-      if (!all_kept) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = rb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-          const bool ok = kvalid & (off < rrem) & (!p.causal | (hi + off >= 0)) & ((lo + off <= 0) | k_sink);
-          sc[r] = ok ? sc[r] : -INFINITY;
-        }
-      }
-      // P and dS with the statistics of each element's row
+    };
+    // P = exp2(S·sigma·log2 e - LSE·log2 e), dS = P (dP - D), bf16 B operands
+    auto softmax = [&](HalfAcc& c, const HalfSt& t, HalfB& b) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int row = rb * 32 + r4 * 8 + h * 4;
-        const f32x4 a = *reinterpret_cast<const f32x4*>(ss + SC::stat_off(row));
-        const f32x4 c = *reinterpret_cast<const f32x4*>(ss + SC::stat_off(row) + 4);
-        const float l2[4] = {a[0], a[2], c[0], c[2]};
-        const float dd[4] = {a[1], a[3], c[1], c[3]};
+        const float l2[4] = {t.a[r4][0], t.a[r4][2], t.c[r4][0], t.c[r4][2]};
+        const float dd[4] = {t.a[r4][1], t.a[r4][3], t.c[r4][1], t.c[r4][3]};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[4 * r4 + e], p.scale_log2, -l2[e]));
-          sc[4 * r4 + e] = pr;
-          dp[4 * r4 + e] = pr * (dp[4 * r4 + e] - dd[e]);
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(c.s[4 * r4 + e], p.scale_log2, -l2[e]));
+          c.s[4 * r4 + e] = pr;
+          c.dp[4 * r4 + e] = pr * (c.dp[4 * r4 + e] - dd[e]);
         }
       }
-      bf16x8 pf[2], dsf[2];
-      pack_half(sc, pf);
-      pack_half(dp, dsf);
+      pack_half(c.s, b.p);
+      pack_half(c.dp, b.ds);
+    };
+    // Two halves of 32 rows: S, dP, then dV, dK over those rows.  With one
+    // wave per SIMD nothing else hides LDS latency, so each phase's operand
+    // reads are issued before its MFMAs (sched_barrier keeps them there), and
+    // the transposing reads and row statistics fly during the S/dP MFMAs.
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(to.tr_op(gs, db, 2 * rb + k2), pf[k2], dvacc[db],
-                                                              0, 0, 0);
-          dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(to.tr_op(qs, db, 2 * rb + k2), dsf[k2],
-                                                              dkacc[db], 0, 0, 0);
-        }
+    for (int rb = 0; rb < 2; ++rb) {
+      HalfOps a;
+      HalfAcc c;
+      HalfTr t;
+      HalfSt st;
+      HalfB b;
+      load_rows(a, rb);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_sdp(a, c);
+      load_tr(t, rb);
+      load_stats(st, rb);
+      __builtin_amdgcn_sched_barrier(0);
+      if (!all_kept) mask(c, rb);
+      softmax(c, st, b);
+      mfma_grad(t, b);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (pre)
       stage_barrier<kLoads>();
