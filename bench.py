@@ -32,11 +32,15 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense bf16/f16 M
 PEAK_HBM_GBS = 8000.0
 METRIC = "causal attn TFLOP/s + % bf16 MFMA peak, 70B-shape GQA layer at 128K ctx"
 PMC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_llama3_70b_128k_pmc.json")
-KERNEL_SRC = os.path.join(ROOT, "long_context_attention_rope_amd", "csrc", "attn_fwd.hip")
+KERNEL_SRC = [os.path.join(ROOT, "long_context_attention_rope_amd", "csrc", f)
+              for f in ("attn_fwd.hip", "attn_tile.h")]  # the attention kernel's source text
 
 
 def kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SRC:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(launch_flop_bytes):
@@ -360,13 +364,13 @@ def main():
     ap.add_argument("--v-layout", choices=["tiles", "rows"], default="tiles",
                     help="V packed into 64-key tiles by lcx_attn_pack_v inside the step (default) or read as rows")
     ap.add_argument("--cpu-rows", type=int, default=None,
-                    help="oracle rows for the CPU baseline (default 2048; 640 for the chunked workload; 0: skip)")
+                    help="oracle rows for the CPU baseline (default 16384; 640 for the chunked workload; 0: skip)")
     ap.add_argument("--decode", type=int, default=0, metavar="N",
                     help="time split-KV decode of N new rows (1..8) against this layer's cache instead")
     ap.add_argument("--splits", type=int, default=None, help="decode: workgroups per KV head")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass (lcx_attn_bwd) of this layer instead; --cpu-rows is then "
-                         "the length of the prefix the oracle differentiates (default 2560)")
+                         "the length of the prefix the oracle differentiates (default 5120)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-merge-check", dest="merge_check", action="store_false",
                     help="skip timing the merge pass on this layer's partial sizes")
@@ -394,7 +398,7 @@ def main():
     if args.warmup is None:
         args.warmup = 1 if w.chunk else 3
     if args.cpu_rows is None:
-        args.cpu_rows = 640 if w.chunk else (2560 if args.bwd else 2048)
+        args.cpu_rows = 640 if w.chunk else (5120 if args.bwd else 16384)
     if args.bwd:
         return bench_backward(args, w)
     if w.chunk:

@@ -22,18 +22,22 @@
 //    S^T = K·Q^T and dP^T = V·dO^T take row reads of the K and V tiles;
 //    P and dS are formed in the accumulator layout, and dQ^T += K^T·dS^T
 //    takes transposing reads of the same K tile.
-//  * bwd_dkdv, key-stationary: a wave keeps 32 keys' k~ and v in registers
+//  * bwd_dkdv, key-stationary: a wave keeps 16 keys' k~ and v in registers
 //    and walks the 64-row tiles of q~, dO and the row statistics of every
 //    query head of its KV head that keeps those keys.  S = Q·K^T and
 //    dP = dO·V^T take row reads; dV^T += dO^T·P and dK^T += Q^T·dS take
 //    transposing reads.  The G heads of the group are summed in registers,
-//    so every dk, dv row is written once (no atomics).
-//  * Every product is v_mfma_f32_32x32x16_bf16 with fp32 accumulation: q~
-//    and k~ come in bf16, and P and dS are rounded to bf16 (dS needs bf16's
-//    exponent range: its entries shrink with the row length).
-//  * One LDS swizzle serves both the row reads (one 16-byte chunk of each
-//    of 16 consecutive rows per 16 lanes) and the transposing reads (4 chunks
-//    of 4 consecutive rows per 32 lanes) without bank conflicts.
+//    so every dk, dv row is written once (no atomics).  16 keys per wave on
+//    v_mfma_f32_16x16x32_bf16 keep the stationary state at 96 registers, so
+//    two waves share each SIMD (with 32 keys on 32x32x16 it took 460
+//    registers, one wave per SIMD, and nothing hid its softmax and latency).
+//  * The dq products are v_mfma_f32_32x32x16_bf16.  All products take bf16
+//    operands with fp32 accumulation: q~ and k~ come in bf16, and P and dS
+//    are rounded to bf16 (dS needs bf16's exponent range: its entries shrink
+//    with the row length).
+//  * Each kernel's tile swizzle serves both its row reads (one 16-byte chunk
+//    of each of 16 consecutive rows per 16 lanes) and its transposing reads
+//    without LDS bank conflicts.
 //  * Tiles are copied global -> LDS with no register round trip, three
 //    stages deep, one barrier per step (as in the forward).
 #include "attn_tile.h"
@@ -56,12 +60,25 @@ __device__ __forceinline__ int b_swz(int r) {
 }
 
 // Copy of the 64-row tile at rows j0 .. j0+63 of a [rows][D] bf16 matrix
-// (row stride rs elements) into LDS, row r's chunk c in slot c ^ b_swz(r):
+// (row stride rs elements) into LDS, row r's chunk c in slot c ^ swz(r):
 // per wave LPW loads, lane L of load i fills row (wave·LPW + i)·RPL + L/CPR,
 // slot L % CPR.  The resource ends at the last existing row (rows past it
 // land as zeros) and spans at most one tile, so any row stride below 2^25
 // elements keeps offsets in 32 bits.
-template <int D, int NW>
+// Tiles of the 16-key dK/dV kernel: its transposing reads take 2 chunks of 8
+// consecutive rows per 32 lanes, so (c ^ s_swz(r)) >> 1 differs over 8
+// consecutive rows; its row reads still see 16 distinct slots over 16 rows.
+template <int D>
+__device__ __forceinline__ int s_swz(int r) {
+  return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+}
+
+template <int D, bool S16>
+__device__ __forceinline__ int tile_swz(int r) {
+  return S16 ? s_swz<D>(r) : b_swz<D>(r);
+}
+
+template <int D, int NW, bool S16 = false>
 struct TileCopy {
   static constexpr int CPR = D / 8;
   static constexpr int RPL = 1024 / (2 * D);
@@ -87,28 +104,24 @@ struct TileCopy {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int row = row0 + i * RPL + lane / CPR;
-      const uint32_t off = (uint32_t)(row * rs * 2) + (uint32_t)(((lane % CPR) ^ b_swz<D>(row)) * 16);
+      const uint32_t off = (uint32_t)(row * rs * 2) + (uint32_t)(((lane % CPR) ^ tile_swz<D, S16>(row)) * 16);
       const uint32_t la = (uint32_t)(uintptr_t)(lds_void*)(lds + (row0 + i * RPL) * D);
       lds_copy16(r, off, __builtin_amdgcn_readfirstlane(la));
     }
   }
 };
 
-// Row statistics (LSE·log2 e, D) of a 64-row tile into LDS: wave w copies
-// rows 64/NW·w .. (one load, its first 64/NW/2 lanes in range) into its own
-// 1 KB region.  Row r of the tile is at float offset stat_off(r).
-template <int NW>
-struct StatsCopy {
-  static constexpr int RW = BN / NW;  // rows per wave
-  static constexpr int REGION = 256;  // floats per wave region (64 lanes x 16 B)
-  __device__ static __forceinline__ int stat_off(int r) { return (r / RW) * REGION + (r % RW) * 2; }
+// Row statistics of a 64-row tile copied by one wave: 64 rows x 8 bytes,
+// lanes 0-31 in range (lanes past the last row land as zeros); row r at
+// float offset 2r.
+struct StatsCopy1 {
+  static constexpr int FLOATS = 256;  // LDS floats per stage (64 lanes x 16 B)
   __device__ static __forceinline__ void issue(float* lds, const float* rows_base, int64_t n_rows,
-                                               int64_t j0, int wave, int lane) {
-    const int64_t first = j0 + wave * RW;
-    const int64_t left = n_rows - first;
-    const uint32_t rows = left <= 0 ? 0u : (left >= RW ? (uint32_t)RW : (uint32_t)left);
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(rows_base + 2 * first, rows * 8u);
-    const uint32_t la = (uint32_t)(uintptr_t)(lds_void*)(lds + wave * REGION);
+                                               int64_t j0, int lane) {
+    const int64_t left = n_rows - j0;
+    const uint32_t rows = left <= 0 ? 0u : (left >= BN ? (uint32_t)BN : (uint32_t)left);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(rows_base + 2 * j0, rows * 8u);
+    const uint32_t la = (uint32_t)(uintptr_t)(lds_void*)lds;
     lds_copy16(r, (uint32_t)lane * 16u, __builtin_amdgcn_readfirstlane(la));
   }
 };
@@ -424,12 +437,25 @@ __device__ __forceinline__ KeyBlock key_block(const BwdParams& p) {
   return kb;
 }
 
+// dK, dV on v_mfma_f32_16x16x32_bf16 with 16 keys per wave: the stationary
+// state (k~, v fragments and the dK^T, dV^T accumulators) is 96 registers for
+// d = 128, so two waves share each SIMD and hide each other's softmax and LDS
+// latency.  Layouts (lane l, i = l % 16, g = l / 16):
+//   A operand  lane holds A[i][8g .. 8g+7]
+//   B operand  lane holds B[8g .. 8g+7][i]
+//   C/D        register r of lane holds C[4g + r][i]
+// S = Q·K^T per 16-row block rb: A = q~ rows (row 16rb + i, chunk 4c + g),
+// B = k~ of key i; the accumulator gives key i, rows 16rb + 4g + r.  The B
+// operand of dV^T += dO^T·P over the 32 rows of half kc is then registers
+// 0-3 of blocks 2kc and 2kc+1: rows 32kc + 4g + {0..3} and 32kc + 16 + 4g +
+// {0..3}; the A operand dO^T holds the same rows of column 16db + i, two
+// transposing reads (lane j of group g reads row 32kc + 4g + j/4, and 16
+// below, columns 16db + 4(j % 4) .. +3).
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p) {
-  using C = TileCopy<D, NW>;
-  using SC = StatsCopy<NW>;
+  using C = TileCopy<D, NW, true>;
   constexpr int TE = BN * D;
-  constexpr int SE = NW * SC::REGION;
+  constexpr int SE = StatsCopy1::FLOATS;
   __shared__ __attribute__((aligned(1024))) uint16_t q_st[3][TE];
   __shared__ __attribute__((aligned(1024))) uint16_t g_st[3][TE];
   __shared__ __attribute__((aligned(1024))) float s_st[3][SE];
@@ -437,41 +463,60 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31;
-  const int h = lane >> 5;
+  const int i16 = lane & 15;
+  const int g = lane >> 4;
 
-  const KeyBlock kb = key_block<32 * NW>(p);
-  const int nrt = kb.t_hi - kb.t_lo;  // row tiles per head
+  const KeyBlock kb = key_block<16 * NW>(p);
+  const int nrt = kb.t_hi - kb.t_lo;
   const int nsteps = nrt * p.G;
-  const int64_t wkey0 = kb.key0 + 32 * wave;  // this wave's first key
-  const int64_t key = wkey0 + l32;            // this lane's key
+  const int64_t wkey0 = kb.key0 + 16 * wave;
+  const int64_t key = wkey0 + i16;
   const bool kvalid = key < p.n_kv;
   const int64_t kpos = p.k_pos0 + key;
 
-  bf16x8 kf[D / 16], vf[D / 16];
-  load_frag<D>(p.k + kb.b * p.ks_b + kb.hkv * p.ks_h, key, kvalid, p.ks_s, h, kf);
-  load_frag<D>(p.v + kb.b * p.vs_b + kb.hkv * p.vs_h, key, kvalid, p.vs_s, h, vf);
-
-  f32x16 dkacc[D / 32], dvacc[D / 32];
+  // B operands of S and dP: key i16's elements 32c + 8g .. +7
+  bf16x8 kf[D / 32], vf[D / 32];
+  {
+    const uint16_t* kbase = p.k + kb.b * p.ks_b + kb.hkv * p.ks_h + key * p.ks_s;
+    const uint16_t* vbase = p.v + kb.b * p.vs_b + kb.hkv * p.vs_h + key * p.vs_s;
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i)
+    for (int c = 0; c < D / 32; ++c) {
+      u32x4 rk = {0u, 0u, 0u, 0u}, rv = {0u, 0u, 0u, 0u};
+      if (kvalid) {
+        rk = *reinterpret_cast<const u32x4*>(kbase + 32 * c + 8 * g);
+        rv = *reinterpret_cast<const u32x4*>(vbase + 32 * c + 8 * g);
+      }
+      kf[c] = __builtin_bit_cast(bf16x8, rk);
+      vf[c] = __builtin_bit_cast(bf16x8, rv);
+    }
+  }
+  f32x4 dkacc[D / 16], dvacc[D / 16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dkacc[i][r] = 0.f;
-      dvacc[i][r] = 0.f;
+  for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      dkacc[db][r] = 0.f;
+      dvacc[db][r] = 0.f;
     }
 
-  // per-wave mask facts that do not depend on the row tile
-  const bool keys_whole = wkey0 + 32 <= p.n_kv;
-  const int64_t wkpos_min = p.k_pos0 + wkey0, wkpos_max = wkpos_min + 31;
+  const bool keys_whole = wkey0 + 16 <= p.n_kv;
+  const int64_t wkpos_min = p.k_pos0 + wkey0, wkpos_max = wkpos_min + 15;
   const bool k_sink = kpos < (int64_t)p.n_sink;
 
-  TileOffsets<D> to;
-  to.init(lane);
+  // per-lane LDS offsets: row reads and the first transposing read
+  int roff[D / 32], toff[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) roff[c] = i16 * D + 8 * ((4 * c + g) ^ s_swz<D>(i16));
+  {
+    const int r0 = 4 * g + (i16 >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+      toff[db] = r0 * D + 8 * ((2 * db + ((i16 & 3) >> 1)) ^ s_swz<D>(r0)) + 4 * (i16 & 1);
+  }
+
   C qcp, gcp;
   qcp.init(p.qs_s, p.n_q, wave, lane);
   gcp.init(p.dos_s, p.n_q, wave, lane);
-  // step s: row tile t_hi - 1 - s / G (last rows first), query head hkv·G + s % G
   auto step_rows = [&](int s) -> int64_t { return (int64_t)(kb.t_hi - 1 - s / p.G) * BN; };
   auto step_head = [&](int s) -> int { return kb.hkv * p.G + s % p.G; };
   auto issue = [&](uint16_t* qs, uint16_t* gs, float* ss, int s) {
@@ -479,69 +524,17 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
     const int hq = step_head(s);
     qcp.issue(qs, p.q + kb.b * p.qs_b + hq * p.qs_h, j0);
     gcp.issue(gs, p.dout + kb.b * p.dos_b + hq * p.dos_h, j0);
-    SC::issue(ss, p.stats + 2 * ((int64_t)kb.b * p.Hq + hq) * p.n_q, p.n_q, j0, wave, lane);
+    // the statistics come with wave 0's copies (one 512-byte load instead
+    // of one small load per wave)
+    if (wave == 0) StatsCopy1::issue(ss, p.stats + 2 * ((int64_t)kb.b * p.Hq + hq) * p.n_q, p.n_q, j0, lane);
   };
-  constexpr int kLoads = 2 * C::LPW + 1;
-
-  // per-half registers of the step pipeline
-  struct HalfOps { bf16x8 q[D / 16], g[D / 16]; };          // row operands (A of S, dP)
-  struct HalfAcc { f32x16 s, dp; };                          // S, dP accumulators
-  struct HalfTr { bf16x8 g[D / 32][2], q[D / 32][2]; };      // transposed operands (A of dV, dK)
-  struct HalfSt { f32x4 a[4], c[4]; };                       // (LSE·log2 e, D) of the half's rows
-  struct HalfB { bf16x8 p[2], ds[2]; };                      // B operands of dV, dK
+  constexpr int kLoads = 2 * C::LPW;  // vector memory ops per step (wave 0: one more)
 
   auto step = [&](const uint16_t* qs, const uint16_t* gs, const float* ss, uint16_t* qs_n, uint16_t* gs_n,
                   float* ss_n, int s) {
     const bool pre = s + 2 < nsteps;
     if (pre) issue(qs_n, gs_n, ss_n, s + 2);
     const int64_t j0 = step_rows(s);
-    auto load_rows = [&](HalfOps& a, int rb) {
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        a.q[c] = to.row_op(qs, rb, c);
-        a.g[c] = to.row_op(gs, rb, c);
-      }
-    };
-    auto mfma_sdp = [&](const HalfOps& a, HalfAcc& c) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        c.s[r] = 0.f;
-        c.dp[r] = 0.f;
-      }
-#pragma unroll
-      for (int k = 0; k < D / 16; ++k) {
-        c.s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.q[k], kf[k], c.s, 0, 0, 0);
-        c.dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.g[k], vf[k], c.dp, 0, 0, 0);
-      }
-    };
-    auto load_tr = [&](HalfTr& t, int rb) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          t.g[db][k2] = to.tr_op(gs, db, 2 * rb + k2);
-          t.q[db][k2] = to.tr_op(qs, db, 2 * rb + k2);
-        }
-    };
-    auto load_stats = [&](HalfSt& t, int rb) {
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int row = rb * 32 + r4 * 8 + h * 4;
-        t.a[r4] = *reinterpret_cast<const f32x4*>(ss + SC::stat_off(row));
-        t.c[r4] = *reinterpret_cast<const f32x4*>(ss + SC::stat_off(row) + 4);
-      }
-    };
-    auto mfma_grad = [&](const HalfTr& t, const HalfB& b) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t.g[db][k2], b.p[k2], dvacc[db], 0, 0, 0);
-          dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t.q[db][k2], b.ds[k2], dkacc[db], 0, 0, 0);
-        }
-    };
-    // mask facts of this tile: element (rb, r) is row 32rb + (r/4)·8 + 4h + r%4
-    // of the tile and the lane's key
     const int64_t qpos_t = p.q_pos0 + j0;
     const bool all_kept = keys_whole && (j0 + BN <= p.n_q) && (!p.causal || qpos_t >= wkpos_max) &&
                           (p.window < 0 || qpos_t + BN - 1 - p.window <= wkpos_min ||
@@ -549,57 +542,80 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
     const int hi = clamp_i32(qpos_t - kpos);  // causal: row off kept iff hi + off >= 0
     const int lo = p.window >= 0 ? clamp_i32(qpos_t - kpos - p.window) : -(1 << 30);  // lo + off <= 0
     const int rrem = clamp_tile(p.n_q - j0);
-    // mask of a tile that straddles an edge: -inf scores
-    auto mask = [&](HalfAcc& c, int rb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int off = rb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-        const bool ok = kvalid & (off < rrem) & (!p.causal | (hi + off >= 0)) & ((lo + off <= 0) | k_sink);
-        c.s[r] = ok ? c.s[r] : -INFINITY;
-      }
-    };
-    // P = exp2(S·sigma·log2 e - LSE·log2 e), dS = P (dP - D), bf16 B operands
-    auto softmax = [&](HalfAcc& c, const HalfSt& t, HalfB& b) {
+    for (int kc = 0; kc < 2; ++kc) {
+      // S, dP for row blocks 2kc, 2kc+1
+      f32x4 sc[2], dp[2];
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const float l2[4] = {t.a[r4][0], t.a[r4][2], t.c[r4][0], t.c[r4][2]};
-        const float dd[4] = {t.a[r4][1], t.a[r4][3], t.c[r4][1], t.c[r4][3]};
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(c.s[4 * r4 + e], p.scale_log2, -l2[e]));
-          c.s[4 * r4 + e] = pr;
-          c.dp[4 * r4 + e] = pr * (c.dp[4 * r4 + e] - dd[e]);
+        for (int r = 0; r < 4; ++r) {
+          sc[u][r] = 0.f;
+          dp[u][r] = 0.f;
         }
-      }
-      pack_half(c.s, b.p);
-      pack_half(c.dp, b.ds);
-    };
-    // Two halves of 32 rows: S, dP, then dV, dK over those rows.  With one
-    // wave per SIMD nothing else hides LDS latency, so each phase's operand
-    // reads are issued before its MFMAs (sched_barrier keeps them there), and
-    // the transposing reads and row statistics fly during the S/dP MFMAs.
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      HalfOps a;
-      HalfAcc c;
-      HalfTr t;
-      HalfSt st;
-      HalfB b;
-      load_rows(a, rb);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_sdp(a, c);
-      load_tr(t, rb);
-      load_stats(st, rb);
-      __builtin_amdgcn_sched_barrier(0);
-      if (!all_kept) mask(c, rb);
-      softmax(c, st, b);
-      mfma_grad(t, b);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int rb = 2 * kc + u;
+          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qs + rb * 16 * D + roff[c]);
+          const bf16x8 ag = *reinterpret_cast<const bf16x8*>(gs + rb * 16 * D + roff[c]);
+          sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, kf[c], sc[u], 0, 0, 0);
+          dp[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, vf[c], dp[u], 0, 0, 0);
+        }
+      // element (u, r) is row 32kc + 16u + 4g + r of the tile and the lane's key
+      if (!all_kept) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int off = 32 * kc + 16 * u + 4 * g + r;
+            const bool ok = kvalid & (off < rrem) & (!p.causal | (hi + off >= 0)) & ((lo + off <= 0) | k_sink);
+            sc[u][r] = ok ? sc[u][r] : -INFINITY;
+          }
+      }
+      // P = exp2(S·sigma·log2 e - LSE·log2 e), dS = P (dP - D)
+      u32x4 wp, wd;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int row = 32 * kc + 16 * u + 4 * g;
+        const f32x4 ta = *reinterpret_cast<const f32x4*>(ss + 2 * row);
+        const f32x4 tc = *reinterpret_cast<const f32x4*>(ss + 2 * row + 4);
+        const float l2[4] = {ta[0], ta[2], tc[0], tc[2]};
+        const float dd[4] = {ta[1], ta[3], tc[1], tc[3]};
+        float pr[4], ds[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][r], p.scale_log2, -l2[r]));
+          ds[r] = pr[r] * (dp[u][r] - dd[r]);
+        }
+        wp[2 * u] = pack_bf16x2(pr[0], pr[1]);
+        wp[2 * u + 1] = pack_bf16x2(pr[2], pr[3]);
+        wd[2 * u] = pack_bf16x2(ds[0], ds[1]);
+        wd[2 * u + 1] = pack_bf16x2(ds[2], ds[3]);
+      }
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, wp);
+      const bf16x8 dsf = __builtin_bit_cast(bf16x8, wd);
+      // dV^T += dO^T·P, dK^T += Q^T·dS over the half's 32 rows
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const int o0 = toff[db] + kc * 32 * D;
+        const v4i16 g0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(gs + o0));
+        const v4i16 g1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(gs + o0 + 16 * D));
+        const v4i16 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(qs + o0));
+        const v4i16 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(qs + o0 + 16 * D));
+        const bf16x8 ga = __builtin_bit_cast(bf16x8, __builtin_shufflevector(g0, g1, 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 qa = __builtin_bit_cast(bf16x8, __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7));
+        dvacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga, pf, dvacc[db], 0, 0, 0);
+        dkacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, dsf, dkacc[db], 0, 0, 0);
+      }
     }
-    if (pre)
-      stage_barrier<kLoads>();
-    else
+    if (!pre)
       stage_barrier<0>();
+    else if (wave == 0)
+      stage_barrier<kLoads + 1>();
+    else
+      stage_barrier<kLoads>();
   };
 
   if (nsteps > 0) issue(q_st[0], g_st[0], s_st[0], 0);
@@ -623,22 +639,18 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
     dvd = static_cast<uint16_t*>(p.dv) + kb.b * p.dvs_b + kb.hkv * p.dvs_h + key * p.dvs_s;
   }
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int d0 = db * 32 + r4 * 8 + h * 4;
-      const f32x4 xk = {dkacc[db][4 * r4] * p.scale, dkacc[db][4 * r4 + 1] * p.scale,
-                        dkacc[db][4 * r4 + 2] * p.scale, dkacc[db][4 * r4 + 3] * p.scale};
-      const f32x4 xv = {dvacc[db][4 * r4], dvacc[db][4 * r4 + 1], dvacc[db][4 * r4 + 2],
-                        dvacc[db][4 * r4 + 3]};
-      store4(p, dkd, kpos, d0, xk, p.unrotate != 0);
-      store4(p, dvd, kpos, d0, xv, false);
-    }
+  for (int db = 0; db < D / 16; ++db) {
+    const int d0 = db * 16 + g * 4;
+    const f32x4 xk = {dkacc[db][0] * p.scale, dkacc[db][1] * p.scale, dkacc[db][2] * p.scale,
+                      dkacc[db][3] * p.scale};
+    store4(p, dkd, kpos, d0, xk, p.unrotate != 0);
+    store4(p, dvd, kpos, d0, dvacc[db], false);
+  }
 }
 
 constexpr int kBwdNWq128 = 8;  // dq kernel waves (32 rows each)
 constexpr int kBwdNWq64 = 4;
-constexpr int kBwdNWk = 4;     // dk/dv kernel waves (32 keys each)
+constexpr int kBwdNWk = 8;     // dk/dv kernel waves (16 keys each)
 
 template __global__ void bwd_stats_kernel<64>(const BwdParams);
 template __global__ void bwd_stats_kernel<128>(const BwdParams);
@@ -669,7 +681,7 @@ hipError_t launch_bwd_d(const BwdParams& p_in, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   // dk, dv (every key; with no rows they are zeros)
-  const int64_t kblk = (p.n_kv + 32 * kBwdNWk - 1) / (32 * kBwdNWk);
+  const int64_t kblk = (p.n_kv + 16 * kBwdNWk - 1) / (16 * kBwdNWk);
   if (kblk > 0) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, kBwdNWk>), dim3((unsigned)(kblk * p.B * p.Hkv)),
                        dim3(64 * kBwdNWk), 0, s, p);
@@ -681,7 +693,7 @@ hipError_t launch_bwd_d(const BwdParams& p_in, hipStream_t s) {
 }  // namespace
 
 int attn_bwd_rows_per_block(int d) { return 32 * (d == 64 ? kBwdNWq64 : kBwdNWq128); }
-int attn_bwd_keys_per_block(int d) { return 32 * kBwdNWk; }
+int attn_bwd_keys_per_block(int d) { return 16 * kBwdNWk; }
 
 hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t s) {
   if (p.d == 64) return launch_bwd_d<64, kBwdNWq64>(p, s);
