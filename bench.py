@@ -43,6 +43,29 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
+BWD_PMC_FILE = os.path.join(ROOT, "profiles", "attn_bwd_llama3_70b_128k_pmc.json")
+BWD_SRC = os.path.join(ROOT, "long_context_attention_rope_amd", "csrc", "attn_bwd.hip")
+
+
+def bwd_kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in (BWD_SRC, KERNEL_SRC[1]):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def bwd_traffic_from_profile():
+    """HBM bytes of one lcx_attn_bwd call (its three kernels) from the committed
+    counter runs, only if they were taken on the current backward source."""
+    try:
+        rec = json.load(open(BWD_PMC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != bwd_kernel_hash():
+        return None
+    return rec.get("hbm_bytes_per_backward")
+
+
 def traffic_from_profile(launch_flop_bytes):
     """HBM bytes per attention launch from the committed rocprofv3 counter runs,
     only if they were taken on the current kernel source."""
@@ -346,7 +369,7 @@ def bench_backward(args, w):
         "kernels_ms": {"attn_bwd (stats + dq + dk/dv)": round(bwd_ms, 3)},
         "roofline": {"kernel": "attn_bwd (stats + dq + dk/dv launches)", "bound": "mfma",
                      "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": bwd_traffic_from_profile()},
     }
     if args.cpu_rows > 0:
         out["cpu_baseline"] = cpu_baseline_bwd(w, args.cpu_rows)
