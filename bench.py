@@ -233,7 +233,7 @@ def bench_decode(args, w):
     q_pos0 = w.n - n_q
     cos = torch.empty((n_q, w.d // 2), dtype=torch.float32, device=dev)
     sin = torch.empty_like(cos)
-    n_splits = args.splits or max(1, min(-(-512 // (w.B * w.Hkv)), w.n // 256))
+    n_splits = args.splits or lcx.decode_splits(w.B, w.Hkv, w.n, w.d)
     o = torch.empty((w.B, w.Hq, n_q, w.d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.B, w.Hq, n_q), dtype=torch.float32, device=dev)
     o_part = torch.empty((n_splits, w.B, w.Hq, n_q, w.d), dtype=torch.float32, device=dev)
@@ -243,25 +243,29 @@ def bench_decode(args, w):
     def step(ev=None):
         if ev: ev[0].record(stream)
         lcx.rope_freqs(cfg, cos, sin, q_pos0)
+        if ev: ev[1].record(stream)
         lcx.attn_decode(q, k_rot, v_tiles, o, lse, n_splits=n_splits, o_part=o_part, lse_part=lse_part,
                         rope_q=True, cos=cos, sin=sin, tab_pos0=q_pos0, rope=cfg, window=w.window,
                         n_sink=w.n_sink, q_pos0=q_pos0)
-        if ev: ev[1].record(stream)
+        if ev: ev[2].record(stream)
 
     steps = max(args.steps, 50)
     for _ in range(max(args.warmup, 5)):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    ms = float(np.median([e[0].elapsed_time(e[2]) for e in evs]))
+    tab_ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    dec_ms = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
     cache_bytes = w.B * w.Hkv * w.n * w.d * 2 + w.B * w.Hkv * 64 * ((w.n + 63) // 64) * w.d * 2
     io_bytes = w.B * w.Hq * n_q * w.d * (2 + 2) + 2 * n_splits * w.B * w.Hq * n_q * (w.d + 1) * 4
     gbs = (cache_bytes + io_bytes) / (ms * 1e-3) / 1e9
+    dec_gbs = (cache_bytes + io_bytes) / (dec_ms * 1e-3) / 1e9
     out = {
         "metric": "split-KV decode HBM GB/s (K f16 + V bf16 cache read once per step)",
         "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": max(args.warmup, 5),
@@ -271,8 +275,10 @@ def bench_decode(args, w):
                    "head_dim": w.d, "cached_keys": w.n, "new_rows": n_q, "splits_per_kv_head": n_splits,
                    "rope": w.scheme, "v_layout": "tiles"},
         "tokens_per_s": round(w.B * n_q / (ms * 1e-3), 1),
-        "roofline": {"kernel": "attn_decode + combine", "bound": "hbm", "achieved": round(gbs, 1),
-                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+        "kernels_ms": {"rope_table (new rows)": round(tab_ms, 4), "attn_decode + combine": round(dec_ms, 4)},
+        "roofline": {"kernel": "attn_decode + combine (one lcx_attn_decode call)", "bound": "hbm",
+                     "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None},
     }
     print(json.dumps(out), flush=True)
 

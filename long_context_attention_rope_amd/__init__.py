@@ -238,16 +238,24 @@ def attn_fwd(q, k, v, o=None, lse=None, *, rope_q=False, rope_k=False, cos=None,
     return o, lse
 
 
+def decode_splits(B: int, Hkv: int, n_kv: int, d: int) -> int:
+    """Default split-KV factor of attn_decode: 256 workgroups (512 for d = 64) over
+    the B·Hkv heads, with at least 8 KV tiles of 64 keys per split."""
+    wgs = 256 if d == 128 else 512
+    return max(1, min(-(-wgs // (B * Hkv)), n_kv // 512))
+
+
 def attn_decode(q, k, v, o=None, lse=None, *, n_splits=None, o_part=None, lse_part=None,
                 rope_q=False, cos=None, sin=None, tab_pos0=0, rope=None, softmax_scale=0.0, window=-1,
                 n_sink=0, q_pos0=0, k_pos0=0, out_dtype=torch.bfloat16):
     """lcx_attn_decode.  q [B,Hq,n_q<=8,d], k pre-rotated f16 [B,Hkv,n_kv,d], v rows or
-    pack_v tiles.  n_splits defaults to about 512 workgroups over B·Hkv, at most one per
-    4 KV tiles.  Returns (o, lse)."""
+    pack_v tiles.  n_splits defaults to one workgroup per CU (two for d = 64: each holds
+    NST stages of K/V tiles in LDS) over B·Hkv, at least 8 KV tiles per split.  Returns
+    (o, lse)."""
     B, Hq, n_q, d = q.shape
     Hkv, n_kv = k.shape[1], k.shape[2]
     if n_splits is None:
-        n_splits = max(1, min(-(-512 // (B * Hkv)), n_kv // 256))
+        n_splits = decode_splits(B, Hkv, n_kv, d)
     if o is None:
         o = torch.empty((B, Hq, n_q, d), dtype=out_dtype, device=q.device)
     if lse is None:

@@ -595,15 +595,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
 // of one KV head against a long pre-rotated f16 K cache, the visited KV tiles
 // divided among n_splits workgroups per KV head (split-KV).  Row
 // rho = 32·wave + lane % 32 is head g = rho / n_q, position r = rho % n_q, so
-// one K/V tile read from HBM serves every head of the group.  Each workgroup
-// writes an fp32 partial (O, LSE) of its tiles; decode_combine_kernel merges
-// them by log-sum-exp.  Two LDS stages (64 KB) so that two workgroups share a
-// CU.  [CW §3 (the step's base applies to the new rows), §5.3 merge]
-template <int D, int NW, bool VT>
+// one K/V tile read from HBM serves every head of the group; only the
+// ceil(G·n_q / 32) waves that own rows compute, all NW waves share the copies.
+// The step is HBM-bound with little compute per tile, so NST LDS stages keep
+// NST - 1 tiles in flight per workgroup (Little's law: the bytes in flight
+// must cover the memory latency).  Each workgroup writes an fp32 partial
+// (O, LSE) of its tiles; decode_combine_kernel merges them by log-sum-exp.
+// [CW §3 (the step's base applies to the new rows), §5.3 merge]
+template <int D, int NW, bool VT, int NST>
 __global__ __launch_bounds__(64 * NW) void attn_decode_kernel(const AttnParams p, const DecodeParams dp) {
   using T = Tile<D, NW>;
-  __shared__ __attribute__((aligned(1024))) uint16_t k_st0[T::ELEMS], k_st1[T::ELEMS];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_st0[T::ELEMS], v_st1[T::ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_st[NST][T::ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_st[NST][T::ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -612,6 +615,7 @@ __global__ __launch_bounds__(64 * NW) void attn_decode_kernel(const AttnParams p
   const int h2 = lane >> 5;
   const int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
   const int nq = (int)p.n_q;
+  const bool computes = wave * 32 < p.G * nq;  // wave-uniform
 
   const int rho = wave * 32 + l32;
   const bool valid = rho < p.G * nq;
@@ -640,6 +644,8 @@ __global__ __launch_bounds__(64 * NW) void attn_decode_kernel(const AttnParams p
   int koff[D / 16], voff[4];
   operand_offsets<D, VT>(lane, koff, voff);
 
+  constexpr int kLoads = 2 * T::LPW;  // vector memory ops per wave per tile
+  static_assert(kLoads * (NST - 1) <= 63, "outstanding copies must fit vmcnt");
   auto issue = [&](uint16_t* ks, uint16_t* vs, int t) {
     const int j0 = j0_of(t);
     kcp.issue(ks, j0);
@@ -648,28 +654,38 @@ __global__ __launch_bounds__(64 * NW) void attn_decode_kernel(const AttnParams p
     else
       vcp.issue(vs, j0);
   };
-  auto step = [&](const uint16_t* ks, const uint16_t* vs, uint16_t* ks_next, uint16_t* vs_next, int t) {
-    if (t + 1 < ntl) issue(ks_next, vs_next, t + 1);
-    f32x16 s_cur[2];
-    qk_tile<D>(ks, koff, qf, s_cur);
-    rows.mask(p, s_cur, j0_of(t), h2);
-    rows.rescale(rows.tile_max(p, s_cur));
-    bf16x8 pf[4];
-    rows.probs(p, s_cur, pf);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc)
-        rows.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv_operand<D, VT>(vs, voff, db, kc), pf[kc],
-                                                                rows.oacc[db], 0, 0, 0);
-    stage_barrier<0>();
-  };
-  if (ntl > 0) issue(k_st0, v_st0, 0);
+  for (int i = 0; i < NST - 1; ++i)
+    if (i < ntl) issue(k_st[i], v_st[i], i);
   stage_barrier<0>();
-  for (int t = 0; t < ntl; t += 2) {
-    step(k_st0, v_st0, k_st1, v_st1, t);
-    if (t + 1 >= ntl) break;
-    step(k_st1, v_st1, k_st0, v_st0, t + 1);
+  int cur = 0;
+  for (int t = 0; t < ntl; ++t) {
+    // tile t is in stage t % NST; tile t + NST - 1 goes to the stage tile t - 1 used
+    const int nxt = cur == 0 ? NST - 1 : cur - 1;
+    const bool pre = t + NST - 1 < ntl;
+    if (pre) issue(k_st[nxt], v_st[nxt], t + NST - 1);
+    if (computes) {
+      const uint16_t* ks = k_st[cur];
+      const uint16_t* vs = v_st[cur];
+      f32x16 s_cur[2];
+      qk_tile<D>(ks, koff, qf, s_cur);
+      rows.mask(p, s_cur, j0_of(t), h2);
+      rows.rescale(rows.tile_max(p, s_cur));
+      bf16x8 pf[4];
+      rows.probs(p, s_cur, pf);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc)
+          rows.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv_operand<D, VT>(vs, voff, db, kc), pf[kc],
+                                                                  rows.oacc[db], 0, 0, 0);
+    }
+    // tile t + 1 landed (the NST - 2 newer tiles may still be in flight)
+    if (pre)
+      stage_barrier<kLoads * (NST - 2)>();
+    else
+      stage_barrier<0>();
+    cur = cur == NST - 1 ? 0 : cur + 1;
   }
 
   // this split's partial, fp32 [B][Hq][n_q][d] and [B][Hq][n_q]
@@ -699,14 +715,14 @@ __global__ __launch_bounds__(64 * NW) void attn_decode_kernel(const AttnParams p
 LCX_ATTN_INST(64, kNWd64)
 LCX_ATTN_INST(128, kNWd128)
 #undef LCX_ATTN_INST
-template __global__ void attn_decode_kernel<64, 1, false>(const AttnParams, const DecodeParams);
-template __global__ void attn_decode_kernel<64, 2, false>(const AttnParams, const DecodeParams);
-template __global__ void attn_decode_kernel<64, 1, true>(const AttnParams, const DecodeParams);
-template __global__ void attn_decode_kernel<64, 2, true>(const AttnParams, const DecodeParams);
-template __global__ void attn_decode_kernel<128, 1, false>(const AttnParams, const DecodeParams);
-template __global__ void attn_decode_kernel<128, 2, false>(const AttnParams, const DecodeParams);
-template __global__ void attn_decode_kernel<128, 1, true>(const AttnParams, const DecodeParams);
-template __global__ void attn_decode_kernel<128, 2, true>(const AttnParams, const DecodeParams);
+// decode: 4 waves (the copies' vector memory ops split four ways), NST stages
+constexpr int kDecNW = 4;
+constexpr int kDecNST128 = 5;  // 5 x 32 KB = all 160 KB of LDS: one workgroup per CU, 4 tiles in flight
+constexpr int kDecNST64 = 4;   // 4 x 16 KB: two workgroups per CU
+template __global__ void attn_decode_kernel<64, kDecNW, false, kDecNST64>(const AttnParams, const DecodeParams);
+template __global__ void attn_decode_kernel<64, kDecNW, true, kDecNST64>(const AttnParams, const DecodeParams);
+template __global__ void attn_decode_kernel<128, kDecNW, false, kDecNST128>(const AttnParams, const DecodeParams);
+template __global__ void attn_decode_kernel<128, kDecNW, true, kDecNST128>(const AttnParams, const DecodeParams);
 
 template <int D, int NW, bool VT>
 hipError_t launch_dv(const AttnParams& p, hipStream_t s, unsigned grid) {
@@ -729,17 +745,18 @@ hipError_t launch_dn(const AttnParams& p, hipStream_t s, unsigned grid) {
 int attn_rows_per_block(int d) { return 32 * (d == 64 ? kNWd64 : kNWd128); }
 
 hipError_t launch_attn_decode(const AttnParams& p, const DecodeParams& dp, hipStream_t s) {
-  const int nw = p.G * (int)p.n_q > 32 ? 2 : 1;
-  const dim3 grid((unsigned)dp.n_splits, (unsigned)p.Hkv, (unsigned)p.B), block(64 * nw);
-#define LCX_DEC(D, NW, VT) hipLaunchKernelGGL((attn_decode_kernel<D, NW, VT>), grid, block, 0, s, p, dp)
+  const dim3 grid((unsigned)dp.n_splits, (unsigned)p.Hkv, (unsigned)p.B), block(64 * kDecNW);
   if (p.d == 64) {
-    if (nw == 1) { if (p.v_tiled) LCX_DEC(64, 1, true); else LCX_DEC(64, 1, false); }
-    else { if (p.v_tiled) LCX_DEC(64, 2, true); else LCX_DEC(64, 2, false); }
+    if (p.v_tiled)
+      hipLaunchKernelGGL((attn_decode_kernel<64, kDecNW, true, kDecNST64>), grid, block, 0, s, p, dp);
+    else
+      hipLaunchKernelGGL((attn_decode_kernel<64, kDecNW, false, kDecNST64>), grid, block, 0, s, p, dp);
   } else {
-    if (nw == 1) { if (p.v_tiled) LCX_DEC(128, 1, true); else LCX_DEC(128, 1, false); }
-    else { if (p.v_tiled) LCX_DEC(128, 2, true); else LCX_DEC(128, 2, false); }
+    if (p.v_tiled)
+      hipLaunchKernelGGL((attn_decode_kernel<128, kDecNW, true, kDecNST128>), grid, block, 0, s, p, dp);
+    else
+      hipLaunchKernelGGL((attn_decode_kernel<128, kDecNW, false, kDecNST128>), grid, block, 0, s, p, dp);
   }
-#undef LCX_DEC
   return hipGetLastError();
 }
 

@@ -164,14 +164,21 @@ hipError_t launch_finalize(const float* o_acc, const float* lse_acc, void* o, in
 
 // Combine of the split-KV decode partials: for each query row, the n_splits
 // (O_s, L_s) pairs (L_s = -inf: a split with no kept key) merge as
-// L = log sum_s e^(L_s), O = sum_s e^(L_s - L) O_s, accumulated with a
-// running maximum.  One workgroup of d/4 threads per row, 16 bytes each.
+// L = log sum_s e^(L_s), O = sum_s e^(L_s - L) O_s, taken about the largest
+// L_s.  One workgroup of 256 threads per row: d/4 column groups of 16 bytes
+// times 256/(d/4) groups of splits, whose independent loads are in flight
+// together; the groups' sums meet in LDS.
 namespace lcx {
 
 namespace {
 
 template <int D>
-__global__ __launch_bounds__(D / 4) void decode_combine_kernel(const AttnParams p, const DecodeParams dp) {
+__global__ __launch_bounds__(256) void decode_combine_kernel(const AttnParams p, const DecodeParams dp) {
+  constexpr int CG = D / 4;     // column groups of 4 floats
+  constexpr int SG = 256 / CG;  // split groups: thread (c, sg) takes splits sg, sg + SG, ...
+  __shared__ float wmax[4];
+  __shared__ f32x4 part[SG][CG];
+  __shared__ float lsum[SG];
   const int64_t row = blockIdx.x;  // (b·Hq + hq)·n_q + r
   const int nq = (int)p.n_q;
   const int r = (int)(row % nq);
@@ -179,36 +186,51 @@ __global__ __launch_bounds__(D / 4) void decode_combine_kernel(const AttnParams 
   const int hq = (int)(bh % p.Hq);
   const int b = (int)(bh / p.Hq);
   const int64_t rows_all = (int64_t)p.B * p.Hq * nq;
-  const int c = threadIdx.x;
-  float m = -INFINITY, l = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < dp.n_splits; ++sp) {
-    const float ls = dp.lse_part[sp * rows_all + row];
-    if (ls == -INFINITY) continue;
-    const f32x4 o = *reinterpret_cast<const f32x4*>(dp.o_part + (sp * rows_all + row) * D + 4 * c);
-    if (ls > m) {
-      const float sc = (m == -INFINITY) ? 0.f : expf(m - ls);
+  const int t = threadIdx.x;
+  const int c = t % CG, sg = t / CG;
+  // the largest partial LSE of the row (the reference for the weights)
+  float m = -INFINITY;
+  for (int sp = t; sp < dp.n_splits; sp += 256) m = fmaxf(m, dp.lse_part[sp * rows_all + row]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] *= sc;
-      l *= sc;
-      m = ls;
-    }
-    const float w = expf(ls - m);
+  for (int off = 32; off >= 1; off /= 2) m = fmaxf(m, __shfl_xor(m, off));
+  if ((t & 63) == 0) wmax[t >> 6] = m;
+  __syncthreads();
+  const float mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  // weighted sums of this thread's splits: independent loads, no running rescale
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float l = 0.f;
+  for (int sp = sg; sp < dp.n_splits; sp += SG) {
+    const float ls = dp.lse_part[sp * rows_all + row];
+    if (ls == -INFINITY) continue;  // an empty partial (also every partial when mx is -inf)
+    const float w = expf(ls - mx);
+    const f32x4 o = *reinterpret_cast<const f32x4*>(dp.o_part + (sp * rows_all + row) * D + 4 * c);
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] += w * o[e];
     l += w;
   }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  part[sg][c] = acc;
+  if (c == 0) lsum[sg] = l;
+  __syncthreads();
+  if (sg != 0) return;
+  f32x4 tot = part[0][c];
+  float lt = lsum[0];
+#pragma unroll
+  for (int i = 1; i < SG; ++i) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tot[e] += part[i][c][e];
+    lt += lsum[i];
+  }
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (p.o_mode == 0) {
     uint16_t* op = static_cast<uint16_t*>(p.o) + b * p.os_b + hq * p.os_h + r * p.os_s + 4 * c;
-    u32x2 w = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+    u32x2 w = {pack_bf16x2(tot[0] * inv, tot[1] * inv), pack_bf16x2(tot[2] * inv, tot[3] * inv)};
     *reinterpret_cast<u32x2*>(op) = w;
   } else {
     float* op = static_cast<float*>(p.o) + b * p.os_b + hq * p.os_h + r * p.os_s + 4 * c;
-    f32x4 w = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    f32x4 w = {tot[0] * inv, tot[1] * inv, tot[2] * inv, tot[3] * inv};
     *reinterpret_cast<f32x4*>(op) = w;
   }
-  if (c == 0) p.lse[b * p.ls_b + hq * p.ls_h + r] = l > 0.f ? m + logf(l) : -INFINITY;
+  if (c == 0) p.lse[b * p.ls_b + hq * p.ls_h + r] = lt > 0.f ? mx + logf(lt) : -INFINITY;
 }
 
 }  // namespace
@@ -217,9 +239,9 @@ hipError_t launch_decode_combine(const AttnParams& p, const DecodeParams& dp, hi
   const int64_t rows = (int64_t)p.B * p.Hq * p.n_q;
   if (rows == 0) return hipSuccess;
   if (p.d == 64)
-    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3((unsigned)rows), dim3(16), 0, s, p, dp);
+    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3((unsigned)rows), dim3(256), 0, s, p, dp);
   else
-    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((unsigned)rows), dim3(32), 0, s, p, dp);
+    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((unsigned)rows), dim3(256), 0, s, p, dp);
   return hipGetLastError();
 }
 
