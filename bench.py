@@ -78,6 +78,28 @@ def traffic_from_profile(launch_flop_bytes):
     return rec.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _single_core(fn, flop_scale):
+    """Rate of fn() on one thread (fn returns (flop, seconds)); threads restored after."""
+    import oracle
+    n = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        flop, dt = fn()
+    finally:
+        oracle.set_num_threads(n)
+    return flop * flop_scale / dt / 1e12
+
+
 def cpu_baseline(w, rows: int):
     import numpy as np
     import fixtures
@@ -91,15 +113,20 @@ def cpu_baseline(w, rows: int):
     q_rows = fixtures.rows_bf16(w.seed, fixtures.Q_ID, flat, w.d)
     k = fixtures.normal_bf16(w.seed, fixtures.K_ID, (w.B, w.Hkv, w.n, w.d))
     v = fixtures.normal_bf16(w.seed, fixtures.V_ID, (w.B, w.Hkv, w.n, w.d))
-    t0 = time.perf_counter()
-    oracle.attn_rows(q_rows, pos, heads, np.zeros(rows, np.int32), k, v, w.Hq, th, pf,
-                     lm / np.sqrt(w.d), True, w.window, w.n_sink)
-    dt = time.perf_counter() - t0
-    flop = 4 * w.d * int(np.sum(pos + 1))
+    def run(n_rows):
+        t0 = time.perf_counter()
+        oracle.attn_rows(q_rows[:n_rows], pos[:n_rows], heads[:n_rows], np.zeros(n_rows, np.int32), k, v,
+                         w.Hq, th, pf, lm / np.sqrt(w.d), True, w.window, w.n_sink)
+        return 4 * w.d * int(np.sum(pos[:n_rows] + 1)), time.perf_counter() - t0
+
+    flop, dt = run(rows)
+    one = _single_core(lambda: run(max(1, rows // 16)), 1.0)
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds": round(dt, 3),
+            "kind": "oracle", "seconds": round(dt, 3), "cpu_model": cpu_model(),
+            "single_core_value": one, "extrapolated_full_layer_s": round(w.flop() / (flop / dt), 1),
             "sample": f"{rows} seeded rows (uniform head, uniform position) of the same layer, "
-                      f"fp64, {flop:.3e} algorithmic FLOP, K rotation of the needed heads included"}
+                      f"fp64, {flop:.3e} algorithmic FLOP, K rotation of the needed heads included; "
+                      f"single core on the first {max(1, rows // 16)} of them"}
 
 
 def copy_calibration(gib: float = 1.0, reps: int = 5):
@@ -297,14 +324,20 @@ def cpu_baseline_bwd(w, m: int):
         return fixtures.rows_bf16(w.seed, tid, flat, w.d).reshape(w.B, H, m, w.d)
     q, g = prefix(fixtures.Q_ID, w.Hq), prefix(fixtures.DO_ID, w.Hq)
     k, v = prefix(fixtures.K_ID, w.Hkv), prefix(fixtures.V_ID, w.Hkv)
-    t0 = time.perf_counter()
-    oracle.attn_bwd(q, k, v, g, th, pf, lm / np.sqrt(w.d), True, w.window, w.n_sink)
-    dt = time.perf_counter() - t0
-    flop = 2.5 * w.with_(n=m).flop()
+    def run(mm):
+        t0 = time.perf_counter()
+        oracle.attn_bwd(q[:, :, :mm], k[:, :, :mm], v[:, :, :mm], g[:, :, :mm], th, pf, lm / np.sqrt(w.d),
+                        True, w.window, w.n_sink)
+        return 2.5 * w.with_(n=mm).flop(), time.perf_counter() - t0
+
+    flop, dt = run(m)
+    one = _single_core(lambda: run(max(1, m // 4)), 1.0)
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds": round(dt, 3),
+            "kind": "oracle", "seconds": round(dt, 3), "cpu_model": cpu_model(),
+            "single_core_value": one, "extrapolated_full_layer_s": round(2.5 * w.flop() / (flop / dt), 1),
             "sample": f"the first {m} positions of all {w.Hq} query heads of the same layer (dq, dk, dv "
-                      f"in full), fp64, {flop:.3e} algorithmic FLOP (5 products per kept pair)"}
+                      f"in full), fp64, {flop:.3e} algorithmic FLOP (5 products per kept pair); single "
+                      f"core on the first {max(1, m // 4)} positions"}
 
 
 def bench_backward(args, w):

@@ -46,6 +46,8 @@ def _load():
             vp, i32, i64, f64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = ctypes.c_int
+            lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+            lib.oracle_set_num_threads.restype = None
             lib.oracle_rope_freqs.argtypes = [ctypes.c_int, f64, ctypes.c_int, i64, i64, i64, f64, f64,
                                               vp, vp, vp, vp]
             lib.oracle_rope_freqs.restype = ctypes.c_int
@@ -67,6 +69,11 @@ def _load():
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the later oracle calls (timing only)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def _c(a, dtype):

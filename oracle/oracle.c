@@ -84,6 +84,15 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads the later calls use (timing only; the results do not depend on it). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* Plain RoPE frequency ladder: theta_i = base^(-2i/d), i = 0 .. d/2-1.
  * [CE] 技術原理 (θ_i = 10000^(-2i/d), each pair (2i, 2i+1) rotated by m·θ_i). */
 static void plain_theta(double base, int d, double* theta) {
