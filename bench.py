@@ -163,7 +163,7 @@ def bench_chunked(args, w):
     cos = torch.empty((w.n, w.d // 2), dtype=torch.float32, device=dev)
     sin = torch.empty_like(cos)
     k_rot = torch.empty(k.shape, dtype=torch.float16, device=dev)
-    v_tiles = torch.empty((w.B, w.Hkv, (w.n + 63) // 64, w.d, 64), dtype=torch.bfloat16, device=dev)
+    v_tiles = torch.empty((w.B, w.Hkv, (w.n + 63) // 64, w.d, 64), dtype=torch.float16, device=dev)
     acc_o = torch.empty((w.B, w.Hq, w.n, w.d), dtype=torch.float32, device=dev)
     acc_l = torch.empty((w.B, w.Hq, w.n), dtype=torch.float32, device=dev)
     o = torch.empty((w.B, w.Hq, w.n, w.d), dtype=torch.bfloat16, device=dev)
@@ -480,7 +480,7 @@ def main():
     cos = torch.empty((w.n, half), dtype=torch.float32, device=dev)
     sin = torch.empty((w.n, half), dtype=torch.float32, device=dev)
     k_rot = torch.empty(k.shape, dtype=torch.float16, device=dev)
-    v_tiles = torch.empty((w.B, w.Hkv, (w.n + 63) // 64, w.d, 64), dtype=torch.bfloat16, device=dev)
+    v_tiles = torch.empty((w.B, w.Hkv, (w.n + 63) // 64, w.d, 64), dtype=torch.float16, device=dev)
     tiled = args.v_layout == "tiles"
     o = torch.empty((w.B, w.Hq, w.n, w.d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.B, w.Hq, w.n), dtype=torch.float32, device=dev)
@@ -564,7 +564,8 @@ def main():
                    "head_dim": w.d, "seq_len": w.n, "rope": w.scheme, "rope_base": w.base,
                    "L_train": w.L_train, "cur_len": w.cur_len, "causal": True,
                    "k_rope": args.k_mode, "v_layout": args.v_layout,
-                   "mfma": "QK^T f16 operands, PV bf16 operands, fp32 accumulate"},
+                   "mfma": ("QK^T f16 operands, PV " + ("f16" if args.v_layout == "tiles" else "bf16")
+                            + " operands, fp32 accumulate")},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
         "kernels_ms": {"rope_table": round(tab_ms, 4), "rope_apply_k": round(rot_ms, 4),

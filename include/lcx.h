@@ -117,7 +117,7 @@ lcx_status lcx_rope_apply_qk(const void* q, void* q_out, const void* k, void* k_
 typedef struct {
   const void* q; /* [B][Hq][n_q][d]; bf16 raw (rope_q = 1) or pre-rotated bf16/f16 */
   const void* k; /* [B][Hkv][n_kv][d]; bf16 raw (rope_k = 1) or pre-rotated bf16/f16 */
-  const void* v; /* [B][Hkv][n_kv][d]; bf16, never rotated; or the tile layout (v_tiled) */
+  const void* v; /* [B][Hkv][n_kv][d]; bf16, never rotated; or f16 tiles (v_tiled) */
   int32_t q_dtype, k_dtype; /* LCX_BF16 or LCX_F16 (F16 only when pre-rotated) */
   int32_t B, Hq, Hkv, d;    /* Hq % Hkv == 0; d in {64, 128} */
   int64_t n_q, n_kv;
@@ -147,8 +147,11 @@ typedef struct {
  * [JJ §4 scaled dot-product attention; CE FlashAttention 的分塊計算策略 (tiles,
  * running max, accumulated output); CE 第二層 (GQA: query head h reads KV head
  * floor(h·Hkv/Hq)); CW §4.1 SWA; CW §4.2 attention sinks].
- * QK^T runs on f16 MFMA (rotated q/k rounded once to f16), PV on bf16 MFMA
- * (P rounded to bf16), fp32 accumulation and softmax.
+ * QK^T runs on f16 MFMA (rotated q scaled by sigma·log2 e and k, each
+ * rounded once to f16: q·sigma·log2 e and k must lie within the f16 range),
+ * PV on f16 MFMA from V tiles (P rounded to f16) or bf16 MFMA from V rows
+ * (P rounded to bf16); fp32 accumulation and softmax, row sums of P rounded
+ * to f16.
  * Errors: INVALID_ARG for NULL q/k/v/o/lse, sizes <= 0 (n_kv may be 0: all
  * rows empty), Hq % Hkv != 0, window < -1, n_sink < 0, tables missing or not
  * covering the rotated positions, accumulate with a bf16 o, f16 with rope on;
@@ -181,12 +184,15 @@ lcx_status lcx_attn_decode(const lcx_attn_args* a, int32_t n_splits, float* o_pa
                            hipStream_t stream);
 
 /*
- * Layout step for the PV product (V is not transformed): V copied into the
- * tile layout that lcx_attn_fwd reads with v_tiled = 1, so that each MFMA
- * operand of O += P·V is one 16-byte LDS read (the same role as the
- * pre-rotation of K by lcx_rope_apply_qk).  [上下文擴充套件 FlashAttention 的分塊計算策略]
+ * Layout step for the PV product (V is not rotated): V converted to f16 and
+ * copied into the tile layout that lcx_attn_fwd reads with v_tiled = 1, so
+ * that each MFMA operand of O += P·V is one 16-byte LDS read and P can be
+ * kept in f16 (the same role as the pre-rotation of K to f16 by
+ * lcx_rope_apply_qk).  [上下文擴充套件 FlashAttention 的分塊計算策略]
+ * The conversion is exact for magnitudes in [2^-14, 65504]; smaller values
+ * keep an absolute precision of 2^-24 and larger ones become infinite.
  *   v        [B][Hkv][n][d] bf16, strides v_strides (elements), rows 16-byte aligned
- *   v_tiles  [B][Hkv][T][d][64] bf16, T = ceil(n / 64), contiguous, caller-owned:
+ *   v_tiles  [B][Hkv][T][d][64] f16, T = ceil(n / 64), contiguous, caller-owned:
  *            tile t, row e holds V[64t + key][e] for the 64 keys of the tile,
  *            the keys of each 16-key group in the order 0-3, 8-11, 4-7, 12-15
  *            (the row order of the QK^T accumulator); keys >= n are zeros.

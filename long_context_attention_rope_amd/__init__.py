@@ -182,7 +182,9 @@ def _attn_args(q, k, v, o, lse, *, rope_q, rope_k, cos, sin, tab_pos0, cfg, soft
     a.B, a.Hq, a.Hkv, a.d = B, Hq, Hkv, d
     a.n_q, a.n_kv = n_q, n_kv
     a.q_strides, a.k_strides = _s3(q), _s3(k)
-    if v.dim() == 5:  # tile layout from pack_v: [B, Hkv, T, d, 64]
+    if v.dim() == 5:  # tile layout from pack_v: [B, Hkv, T, d, 64] f16
+        if v.dtype != torch.float16:
+            raise ValueError("V tiles (pack_v output) are float16")
         a.v_strides = (_i64 * 3)(v.stride(0), v.stride(1), 0)
         a.v_tiled = 1
     else:
@@ -208,14 +210,16 @@ def _attn_args(q, k, v, o, lse, *, rope_q, rope_k, cos, sin, tab_pos0, cfg, soft
 
 
 def pack_v(v, out=None):
-    """lcx_attn_pack_v: v [B,Hkv,n,d] bf16 -> tile layout [B,Hkv,ceil(n/64),d,64] bf16,
-    accepted by attn_fwd / attn_fwd_chunked in place of v."""
+    """lcx_attn_pack_v: v [B,Hkv,n,d] bf16 -> tile layout [B,Hkv,ceil(n/64),d,64] float16
+    (V converted to f16), accepted by attn_fwd / attn_fwd_chunked / attn_decode in place of v."""
     B, Hkv, n, d = v.shape
     T = (n + 63) // 64
+    if v.dtype != torch.bfloat16:
+        raise ValueError("pack_v takes bf16 V")
     if out is None:
-        out = torch.empty((B, Hkv, T, d, 64), dtype=v.dtype, device=v.device)
-    if tuple(out.shape) != (B, Hkv, T, d, 64) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [B, Hkv, T, d, 64] tensor")
+        out = torch.empty((B, Hkv, T, d, 64), dtype=torch.float16, device=v.device)
+    if tuple(out.shape) != (B, Hkv, T, d, 64) or not out.is_contiguous() or out.dtype != torch.float16:
+        raise ValueError("out must be a contiguous float16 [B, Hkv, T, d, 64] tensor")
     _check(_lib.lcx_attn_pack_v(_ptr(v), _ptr(out), B, Hkv, n, d, _s3(v), _stream(v)))
     return out
 

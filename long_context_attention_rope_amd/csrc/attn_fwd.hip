@@ -15,10 +15,11 @@
 //  * S^T = K·Q^T on v_mfma_f32_32x32x16_f16: the 32x32 accumulator of a wave
 //    puts all 32 scores of one query row (for a 32-key block) in lanes l and
 //    l^32, so row max / row sum are in-lane plus one permlane32 swap.
-//  * The S^T accumulator is, after exp2 and bf16 packing, directly the B
-//    operand of O^T += V^T·P^T on v_mfma_f32_32x32x16_bf16; V is transposed
-//    while being staged (key order permuted within each 16-key group to match
-//    the accumulator's row order), so each MFMA operand is one ds_read_b128.
+//  * The S^T accumulator is, after exp2 and 16-bit packing, directly the B
+//    operand of O^T += V^T·P^T.  From V tiles (lcx_attn_pack_v: f16, keys of
+//    each 16-key group in the accumulator's row order) each MFMA operand is
+//    one ds_read_b128 and P is packed to f16 (v_mfma_f32_32x32x16_f16); from
+//    bf16 V rows the operand takes two transposing reads and P is bf16.
 //  * Per tile: S(t) = K(t)·Q^T, softmax, O += V(t)·P(t), with tile t+1's
 //    buffer loads in flight (their range check zero-fills rows past the last
 //    key) and staged into the other LDS buffer at the end; one barrier per
@@ -28,9 +29,14 @@
 //    K is either pre-rotated (f16) or rotated while being staged.
 //  * Rotated q/k are rounded once to f16 (three more mantissa bits than bf16:
 //    it keeps the LSE of short rows within 1e-3), P to bf16.
-//  * Online softmax in base 2 with the scale folded into one FMA; the O
-//    rescale is skipped while the running max grows by less than 2^8
-//    (exact: the final O/l uses the same reference max for both).
+//  * Online softmax in base 2: Q is scaled by sigma·log2(e) before its f16
+//    rounding and the QK^T product starts from -m (the row's reference max)
+//    in the accumulator, so the scores come out ready for exp2 with no
+//    per-element VALU work.  The reference max moves (and O is rescaled)
+//    only when a row's max grows by more than 2^8 (exact: the final O/l uses
+//    the same reference max for both).  Row sums add P rounded to f16 (the
+//    PV operand itself from tiles), two per v_dot2c into a per-tile partial,
+//    then into an fp32 total.
 //  * Tiles entirely outside the causal / window+sink mask are never visited;
 //    only tiles that straddle a mask edge are masked per element (branch-free).
 //  * Block order: longest causal rows first; the G query heads of one KV head
@@ -73,12 +79,14 @@ __device__ __forceinline__ int v_swz(int r) {
 }
 
 // Q fragment for the B operand of S^T = K Q^T: lane (n, h2) holds
-// q[row n][16c + 8h2 .. +7] for c = 0 .. D/16-1, rotated and in f16.
+// q[row n][16c + 8h2 .. +7] for c = 0 .. D/16-1, rotated, scaled by
+// sigma·log2(e) and rounded once to f16.
 template <int D>
 __device__ __forceinline__ void load_q(const AttnParams& p, const uint16_t* qbase, int64_t qi,
                                        int h2, f16x8 (&qf)[D / 16]) {
   const bool valid = qi < p.n_q;
   const int64_t trow = p.q_pos0 + qi - p.tab_pos0;
+  const float sc = p.scale_log2;
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
     const int col = 16 * c + 8 * h2;
@@ -91,11 +99,13 @@ __device__ __forceinline__ void load_q(const AttnParams& p, const uint16_t* qbas
         cs = *reinterpret_cast<const f32x4*>(p.cos_tab + trow * (D / 2) + col / 2);
         sn = *reinterpret_cast<const f32x4*>(p.sin_tab + trow * (D / 2) + col / 2);
       }
-      w = rotate4_bf16<true>(raw, cs, sn);
+      w = rotate4_bf16<true>(raw, cs * sc, sn * sc);
     } else if (p.q_mode == 1) {
-      w = bf16_to_f16_4(raw);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = pack_f16x2(bf16lo(raw[i]) * sc, bf16hi(raw[i]) * sc);
     } else {
-      w = raw;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = pack_f16x2(f16lo(raw[i]) * sc, f16hi(raw[i]) * sc);
     }
     qf[c] = __builtin_bit_cast(f16x8, w);
   }
@@ -240,21 +250,19 @@ struct KRegStage {
   }
 };
 
-// S^T = K·Q^T for one tile: lane (n, h2) reads chunk 2c + h2 of K row 32kb + n
-// (koff[c] holds that row-in-block and swizzled chunk; kb adds 32 rows).
+// S^T = K·Q^T - m for one tile: lane (n, h2) reads chunk 2c + h2 of K row
+// 32kb + n (koff[c] holds that row-in-block and swizzled chunk; kb adds 32
+// rows); the products accumulate onto `init` (-m of the lane's row).
 template <int D>
 __device__ __forceinline__ void qk_tile(const uint16_t* ks, const int (&koff)[D / 16],
-                                        const f16x8 (&qf)[D / 16], f32x16 (&s)[2]) {
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+                                        const f16x8 (&qf)[D / 16], const f32x16& init,
+                                        f32x16 (&s)[2]) {
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const f16x8 a = *reinterpret_cast<const f16x8*>(ks + kb * 32 * D + koff[c]);
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[c], s[kb], 0, 0, 0);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[c], c == 0 ? init : s[kb], 0, 0, 0);
     }
   }
 }
@@ -269,26 +277,48 @@ __device__ __forceinline__ void qk_tile(const uint16_t* ks, const int (&koff)[D 
 // the hardware hands lane i the i-th of them from the four keys; voff[db]
 // holds this lane's swizzled address for kc = 0.
 template <int D, bool VT>
-__device__ __forceinline__ bf16x8 pv_operand(const uint16_t* vt, const int (&voff)[4], int db, int kc) {
+__device__ __forceinline__ u32x4 pv_operand(const uint16_t* vt, const int (&voff)[4], int db, int kc) {
   if constexpr (VT) {
     // tile layout: row 32db + l32 holds the keys already in accumulator order,
     // so the 8 values are chunk 2kc + h2 of that row; voff[kc] is this lane's
     // swizzled address for db = 0
-    return *reinterpret_cast<const bf16x8*>(vt + voff[kc] + db * 32 * BN);
+    return *reinterpret_cast<const u32x4*>(vt + voff[kc] + db * 32 * BN);
   } else {
     const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vt + voff[db] + kc * 16 * D));
     const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vt + voff[db] + (kc * 16 + 8) * D));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+    return __builtin_bit_cast(u32x4, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
   }
+}
+
+// O^T += V^T·P^T over one tile: f16 operands from V tiles, bf16 from V rows
+template <int D, bool VT>
+__device__ __forceinline__ void pv_tile(const uint16_t* vs, const int (&voff)[4], const u32x4 (&pf)[4],
+                                        f32x16 (&oacc)[D / 32]) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const u32x4 a = pv_operand<D, VT>(vs, voff, db, kc);
+      if constexpr (VT)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                          __builtin_bit_cast(f16x8, pf[kc]), oacc[db], 0, 0, 0);
+      else
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                           __builtin_bit_cast(bf16x8, pf[kc]), oacc[db], 0, 0, 0);
+    }
 }
 
 // Online-softmax state and O accumulator of 32 query rows of one head.  Row n
 // is held by lanes n and n + 32: they split the scores of each 32-key block
 // of the S^T accumulator and the d columns of O^T.
-template <int D>
+// KEEP_NEG_M holds the QK^T accumulator's start in 16 registers across tiles;
+// otherwise it is rebuilt from m_run for each tile (for kernels with no
+// registers to spare).
+template <int D, bool PF16, bool KEEP_NEG_M>
 struct Rows32 {
   f32x16 oacc[D / 32];
-  float m_run;  // reference max, log2 units (scaled)
+  f32x16 neg_m;  // -m_use in every element (KEEP_NEG_M)
+  float m_run;  // reference max, log2 units (scaled); -inf before any kept key
   float l_run;  // this lane's partial row sum
   int64_t qi;   // this lane's row
   int64_t qpos, qpos_min, qpos_max;
@@ -300,6 +330,8 @@ struct Rows32 {
       for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
     m_run = -INFINITY;
     l_run = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) neg_m[r] = 0.f;
     qi = row0 + l32;
     qpos = p.q_pos0 + qi;
     const int64_t last = (row0 + 31 < p.n_q ? row0 + 31 : p.n_q - 1);
@@ -316,6 +348,8 @@ struct Rows32 {
       for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
     m_run = -INFINITY;
     l_run = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) neg_m[r] = 0.f;
     qi = row;
     qpos = p.q_pos0 + row;
     qpos_min = qpos_lo;
@@ -347,47 +381,78 @@ struct Rows32 {
         }
     }
   }
-  // row max of a score tile, in scaled log2 units, shared by lanes l and l^32
-  __device__ __forceinline__ float tile_max(const AttnParams& p, const f32x16 (&s)[2]) const {
+  // start of the QK^T accumulator: -m_use, m_use = m_run or 0 before any kept key
+  __device__ __forceinline__ f32x16 qk_init() const {
+    if constexpr (KEEP_NEG_M) {
+      return neg_m;
+    } else {
+      const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
+      f32x16 x;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = nm;
+      return x;
+    }
+  }
+  // row max of a tile of s = S·scale·log2(e) - m_use, shared by lanes l and
+  // l^32 (m_use = m_run, or 0 before any kept key)
+  __device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) const {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    return xor32_max(mx) * p.scale_log2;
+    return xor32_max(mx);
   }
-  // move the reference max when the row max grew by more than 2^kLazyTau
-  __device__ __forceinline__ void rescale(float mx) {
-    const float m_new = fmaxf(m_run, mx);
+  // move the reference max when a row max grew by more than 2^kLazyTau, and
+  // shift this tile's s to the new reference
+  __device__ __forceinline__ void rescale(float mx, f32x16 (&s)[2]) {
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    const float m_new = fmaxf(m_run, m_use + mx);
     if (__any(m_new > m_run + kLazyTau)) {
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      const float alpha = (m_run == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      const float m_next = (m_new == -INFINITY) ? 0.f : m_new;
+      const float shift = m_next - m_use;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] -= shift;
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < D / 32; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) neg_m[r] = -m_next;
     }
   }
-  // P = exp2(S·scale - m) in bf16 (the B operand of PV) and the row sums
-  __device__ __forceinline__ void probs(const AttnParams& p, const f32x16 (&s)[2], bf16x8 (&pf)[4]) {
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+  // P = exp2(s) packed to f16 (PF16) or bf16: the B operand of PV.  The row
+  // sum adds P rounded to f16, two per v_dot2c into a per-tile partial, then
+  // into the fp32 total (f16 keeps the sum of a short row within 2^-11).
+  __device__ __forceinline__ void probs(const f32x16 (&s)[2], u32x4 (&pf)[4]) {
+    const f16x2 one2 = __builtin_bit_cast(f16x2, 0x3c003c00u);
+    float part[2] = {0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float pv[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], p.scale_log2, -m_use));
-        l_run += pv[r];
-      }
+      for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(s[kb][r]);
 #pragma unroll
       for (int hlf = 0; hlf < 2; ++hlf) {
         u32x4 w;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(pv[8 * hlf + 2 * i], pv[8 * hlf + 2 * i + 1]);
-        pf[kb * 2 + hlf] = __builtin_bit_cast(bf16x8, w);
+        for (int i = 0; i < 4; ++i) {
+          // the dot product takes the packed word itself: read back from w, hipcc
+          // (ROCm 7.2) fed element 0 to all four
+          const float p0 = pv[8 * hlf + 2 * i], p1 = pv[8 * hlf + 2 * i + 1];
+          const uint32_t wh = pack_f16x2(p0, p1);
+          part[kb] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, wh), one2, part[kb], false);
+          w[i] = PF16 ? wh : pack_bf16x2(p0, p1);
+        }
+        pf[kb * 2 + hlf] = w;
       }
     }
+    l_run += part[0] + part[1];
   }
   // epilogue: O = O_acc / l, LSE = ln 2 · (m + log2 l); o_mode 2 merges into
   // the existing (O, LSE) partial
@@ -499,7 +564,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
   const uint16_t* kbase = p.k + bt.b * p.ks_b + bt.hkv * p.ks_h;
   const uint16_t* vbase = p.v + bt.b * p.vs_b + bt.hkv * p.vs_h;
 
-  Rows32<D> rows;
+  // the d = 128 kernels that stage K through registers or read V rows have
+  // no 16 registers to spare
+  Rows32<D, VT, D == 64 || (KMODE == 0 && VT)> rows;
   rows.init(p, bt.row0 + wave * 32, l32);
   // Q fragment (RoPE fused here when q_mode == 2)
   f16x8 qf[D / 16];
@@ -543,17 +610,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
       issue(ks_next, vs_next, tn);
     }
     f32x16 s_cur[2];
-    qk_tile<D>(ks, koff, qf, s_cur);
+    qk_tile<D>(ks, koff, qf, rows.qk_init(), s_cur);
     rows.mask(p, s_cur, bt.j0(t), h2);
-    rows.rescale(rows.tile_max(p, s_cur));
-    bf16x8 pf[4];
-    rows.probs(p, s_cur, pf);
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc)
-        rows.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv_operand<D, VT>(vs, voff, db, kc), pf[kc],
-                                                                rows.oacc[db], 0, 0, 0);
+    rows.rescale(rows.tile_max(s_cur), s_cur);
+    u32x4 pf[4];
+    rows.probs(s_cur, pf);
+    pv_tile<D, VT>(vs, voff, pf, rows.oacc);
     if constexpr (KMODE != 0) {
       if (pre) kreg.store(ks_next);
     }
@@ -621,7 +683,7 @@ __global__ __launch_bounds__(64 * NW) void attn_decode_kernel(const AttnParams p
   const bool valid = rho < p.G * nq;
   const int g = valid ? rho / nq : 0;
   const int hq = hkv * p.G + g;
-  Rows32<D> rows;
+  Rows32<D, VT, true> rows;
   rows.init_row(p, valid ? rho - g * nq : nq, p.q_pos0, p.q_pos0 + nq - 1);
   f16x8 qf[D / 16];
   load_q<D>(p, p.q + b * p.qs_b + hq * p.qs_h, rows.qi, h2, qf);
@@ -668,17 +730,12 @@ __global__ __launch_bounds__(64 * NW) void attn_decode_kernel(const AttnParams p
       const uint16_t* ks = k_st[cur];
       const uint16_t* vs = v_st[cur];
       f32x16 s_cur[2];
-      qk_tile<D>(ks, koff, qf, s_cur);
+      qk_tile<D>(ks, koff, qf, rows.qk_init(), s_cur);
       rows.mask(p, s_cur, j0_of(t), h2);
-      rows.rescale(rows.tile_max(p, s_cur));
-      bf16x8 pf[4];
-      rows.probs(p, s_cur, pf);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc)
-          rows.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv_operand<D, VT>(vs, voff, db, kc), pf[kc],
-                                                                  rows.oacc[db], 0, 0, 0);
+      rows.rescale(rows.tile_max(s_cur), s_cur);
+      u32x4 pf[4];
+      rows.probs(s_cur, pf);
+      pv_tile<D, VT>(vs, voff, pf, rows.oacc);
     }
     // tile t + 1 landed (the NST - 2 newer tiles may still be in flight)
     if (pre)

@@ -1,7 +1,8 @@
-// Layout step for the PV product: V [B][Hkv][n][d] (bf16) copied into 64-key
-// tiles [d][64] whose keys are in the row order of the QK^T accumulator, so
-// that the attention kernel reads each PV operand with one 16-byte LDS load.
-// The values are copied bit for bit; keys past n are zeros.
+// Layout step for the PV product: V [B][Hkv][n][d] (bf16) converted to f16
+// (exact for magnitudes in [2^-14, 65504]) into 64-key tiles [d][64] whose
+// keys are in the row order of the QK^T accumulator, so that the attention
+// kernel reads each PV operand with one 16-byte LDS load.  Keys past n are
+// zeros.
 // Source: "上下文擴充套件（Context Extension）" FlashAttention 的分塊計算策略
 // (K/V processed in blocks of B_c keys).
 #include "lcx_device.h"
@@ -40,8 +41,8 @@ __global__ __launch_bounds__(256) void pack_v_kernel(const PackVParams p) {
     u32x4 w;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      w[q] = (uint32_t)tile[tile_key(p0 + 2 * q) * STR + e] |
-             ((uint32_t)tile[tile_key(p0 + 2 * q + 1) * STR + e] << 16);
+      w[q] = pack_f16x2(__uint_as_float((uint32_t)tile[tile_key(p0 + 2 * q) * STR + e] << 16),
+                        __uint_as_float((uint32_t)tile[tile_key(p0 + 2 * q + 1) * STR + e] << 16));
     *reinterpret_cast<u32x4*>(dst + e * kTileKeys + p0) = w;
   }
 }
