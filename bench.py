@@ -294,7 +294,7 @@ def bench_decode(args, w):
     gbs = (cache_bytes + io_bytes) / (ms * 1e-3) / 1e9
     dec_gbs = (cache_bytes + io_bytes) / (dec_ms * 1e-3) / 1e9
     out = {
-        "metric": "split-KV decode HBM GB/s (K f16 + V bf16 cache read once per step)",
+        "metric": "split-KV decode HBM GB/s (K and V cache, 2 B per element, read once per step)",
         "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": max(args.warmup, 5),
         "ms_per_step": round(ms, 4), "wall_ms_per_step": round(wall * 1e3 / steps, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
