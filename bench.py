@@ -66,6 +66,31 @@ def bwd_traffic_from_profile():
     return rec.get("hbm_bytes_per_backward")
 
 
+DEC_PMC_FILE = os.path.join(ROOT, "profiles", "attn_decode_llama3_70b_128k_pmc.json")
+DEC_SRC = [os.path.join(ROOT, "long_context_attention_rope_amd", "csrc", f)
+           for f in ("attn_fwd.hip", "attn_tile.h", "attn_merge.hip")]  # decode + combine kernels
+
+
+def decode_kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in DEC_SRC:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def decode_traffic_from_profile(new_rows, splits):
+    """HBM bytes of one lcx_attn_decode call (decode + combine kernels) from the
+    committed counter runs, only for the same source, new rows and splits."""
+    try:
+        rec = json.load(open(DEC_PMC_FILE))
+    except (OSError, ValueError):
+        return None
+    if (rec.get("kernel_source_sha256_16") != decode_kernel_hash() or rec.get("new_rows") != new_rows
+            or rec.get("splits_per_kv_head") != splits):
+        return None
+    return rec.get("hbm_bytes_per_call")
+
+
 def traffic_from_profile(launch_flop_bytes):
     """HBM bytes per attention launch from the committed rocprofv3 counter runs,
     only if they were taken on the current kernel source."""
@@ -237,7 +262,7 @@ def bench_decode(args, w):
     """Split-KV decode on the layer's KV cache: N new rows (positions n-N .. n-1)
     of all query heads against the n cached keys.  A step = the RoPE table rows
     of the new positions (the base for the current length) + lcx_attn_decode.
-    HBM-bound: the cache (K pre-rotated f16, V tiles bf16) is read once per step."""
+    HBM-bound: the cache (K pre-rotated f16, V f16 tiles) is read once per step."""
     import numpy as np
     import torch
 
@@ -305,7 +330,8 @@ def bench_decode(args, w):
         "kernels_ms": {"rope_table (new rows)": round(tab_ms, 4), "attn_decode + combine": round(dec_ms, 4)},
         "roofline": {"kernel": "attn_decode + combine (one lcx_attn_decode call)", "bound": "hbm",
                      "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                     "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": decode_traffic_from_profile(n_q, n_splits)},
     }
     print(json.dumps(out), flush=True)
 
