@@ -250,18 +250,19 @@ struct KRegStage {
   }
 };
 
-// S^T = K·Q^T - m for one tile: lane (n, h2) reads chunk 2c + h2 of K row
-// 32kb + n (koff[c] holds that row-in-block and swizzled chunk; kb adds 32
-// rows); the products accumulate onto `init` (-m of the lane's row).
-template <int D>
+// S^T = K·Q^T - m for NB 32-key blocks of a tile from block kb0 on: lane
+// (n, h2) reads chunk 2c + h2 of K row 32(kb0 + kb) + n (koff[c] holds that
+// row-in-block and swizzled chunk); the products accumulate onto `init` (-m
+// of the lane's row).
+template <int D, int NB = 2>
 __device__ __forceinline__ void qk_tile(const uint16_t* ks, const int (&koff)[D / 16],
                                         const f16x8 (&qf)[D / 16], const f32x16& init,
-                                        f32x16 (&s)[2]) {
+                                        f32x16 (&s)[NB], int kb0 = 0) {
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const f16x8 a = *reinterpret_cast<const f16x8*>(ks + kb * 32 * D + koff[c]);
+    for (int kb = 0; kb < NB; ++kb) {
+      const f16x8 a = *reinterpret_cast<const f16x8*>(ks + (kb0 + kb) * 32 * D + koff[c]);
       s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[c], c == 0 ? init : s[kb], 0, 0, 0);
     }
   }
@@ -290,15 +291,16 @@ __device__ __forceinline__ u32x4 pv_operand(const uint16_t* vt, const int (&voff
   }
 }
 
-// O^T += V^T·P^T over one tile: f16 operands from V tiles, bf16 from V rows
-template <int D, bool VT>
-__device__ __forceinline__ void pv_tile(const uint16_t* vs, const int (&voff)[4], const u32x4 (&pf)[4],
-                                        f32x16 (&oacc)[D / 32]) {
+// O^T += V^T·P^T over NB 32-key blocks of a tile from block kb0 on (pf[i]
+// holds 16-key chunk 2kb0 + i): f16 operands from V tiles, bf16 from V rows
+template <int D, bool VT, int NB = 2>
+__device__ __forceinline__ void pv_tile(const uint16_t* vs, const int (&voff)[4], const u32x4 (&pf)[2 * NB],
+                                        f32x16 (&oacc)[D / 32], int kb0 = 0) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const u32x4 a = pv_operand<D, VT>(vs, voff, db, kc);
+    for (int kc = 0; kc < 2 * NB; ++kc) {
+      const u32x4 a = pv_operand<D, VT>(vs, voff, db, 2 * kb0 + kc);
       if constexpr (VT)
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                           __builtin_bit_cast(f16x8, pf[kc]), oacc[db], 0, 0, 0);
@@ -355,8 +357,10 @@ struct Rows32 {
     qpos_min = qpos_lo;
     qpos_max = qpos_hi;
   }
-  // mask S(t) (only for tiles that straddle a mask edge for these rows)
-  __device__ __forceinline__ void mask(const AttnParams& p, f32x16 (&s)[2], int j0, int h2) const {
+  // mask S(t), blocks kb0 .. kb0 + NB - 1 (only for tiles that straddle a
+  // mask edge for these rows)
+  template <int NB>
+  __device__ __forceinline__ void mask(const AttnParams& p, f32x16 (&s)[NB], int j0, int h2, int kb0 = 0) const {
     const int64_t kpos_min = p.k_pos0 + j0;
     const int64_t kpos_max = p.k_pos0 + (j0 + BN <= p.n_kv ? j0 + BN : p.n_kv) - 1;
     const bool all_kept = (j0 + BN <= p.n_kv) && (!p.causal || kpos_max <= qpos_min) &&
@@ -372,10 +376,10 @@ struct Rows32 {
       const int srem = clamp_tile((int64_t)p.n_sink - kpos_min);
       const int krem = clamp_tile(p.n_kv - j0);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int off = kb * 32 + (r >> 2) * 8 + h2 * 4 + (r & 3);
+          const int off = (kb0 + kb) * 32 + (r >> 2) * 8 + h2 * 4 + (r & 3);
           const bool ok = (off < krem) & (off <= hi) & ((off >= lo) | (off < srem));
           s[kb][r] = ok ? s[kb][r] : -INFINITY;
         }
@@ -395,17 +399,19 @@ struct Rows32 {
   }
   // row max of a tile of s = S·scale·log2(e) - m_use, shared by lanes l and
   // l^32 (m_use = m_run, or 0 before any kept key)
-  __device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) const {
+  template <int NB>
+  __device__ __forceinline__ float tile_max(const f32x16 (&s)[NB]) const {
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     return xor32_max(mx);
   }
   // move the reference max when a row max grew by more than 2^kLazyTau, and
   // shift this tile's s to the new reference
-  __device__ __forceinline__ void rescale(float mx, f32x16 (&s)[2]) {
+  template <int NB>
+  __device__ __forceinline__ void rescale(float mx, f32x16 (&s)[NB]) {
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     const float m_new = fmaxf(m_run, m_use + mx);
     if (__any(m_new > m_run + kLazyTau)) {
@@ -413,7 +419,7 @@ struct Rows32 {
       const float m_next = (m_new == -INFINITY) ? 0.f : m_new;
       const float shift = m_next - m_use;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] -= shift;
       m_run = m_new;
@@ -429,11 +435,14 @@ struct Rows32 {
   // P = exp2(s) packed to f16 (PF16) or bf16: the B operand of PV.  The row
   // sum adds P rounded to f16, two per v_dot2c into a per-tile partial, then
   // into the fp32 total (f16 keeps the sum of a short row within 2^-11).
-  __device__ __forceinline__ void probs(const f32x16 (&s)[2], u32x4 (&pf)[4]) {
+  template <int NB>
+  __device__ __forceinline__ void probs(const f32x16 (&s)[NB], u32x4 (&pf)[2 * NB]) {
     const f16x2 one2 = __builtin_bit_cast(f16x2, 0x3c003c00u);
-    float part[2] = {0.f, 0.f};
+    float part[NB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < NB; ++kb) part[kb] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
       float pv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(s[kb][r]);
@@ -452,7 +461,10 @@ struct Rows32 {
         pf[kb * 2 + hlf] = w;
       }
     }
-    l_run += part[0] + part[1];
+    if constexpr (NB == 2)
+      l_run += part[0] + part[1];
+    else
+      l_run += part[0];
   }
   // epilogue: O = O_acc / l, LSE = ln 2 · (m + log2 l); o_mode 2 merges into
   // the existing (O, LSE) partial
@@ -655,10 +667,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
 
 // Decode: n_q <= 8 new query rows (positions q_pos0 ..) of all G query heads
 // of one KV head against a long pre-rotated f16 K cache, the visited KV tiles
-// divided among n_splits workgroups per KV head (split-KV).  Row
-// rho = 32·wave + lane % 32 is head g = rho / n_q, position r = rho % n_q, so
-// one K/V tile read from HBM serves every head of the group; only the
-// ceil(G·n_q / 32) waves that own rows compute, all NW waves share the copies.
+// divided among n_splits workgroups per KV head (split-KV).  Waves pair up on
+// 32 rows: row rho = 32·(wave / 2) + lane % 32 is head g = rho / n_q,
+// position r = rho % n_q, so one K/V tile read from HBM serves every head of
+// the group, and the two waves of a pair take the two 32-key halves of each
+// tile (half the per-tile latency on the computing waves), each with its own
+// running (m, l, O), merged through LDS at the end.  Only the pairs that own
+// rows (ceil(G·n_q / 32) <= NW / 2) compute; all NW waves share the copies.
 // The step is HBM-bound with little compute per tile, so NST LDS stages keep
 // NST - 1 tiles in flight per workgroup (Little's law: the bytes in flight
 // must cover the memory latency).  Each workgroup writes an fp32 partial
@@ -677,9 +692,10 @@ __global__ __launch_bounds__(64 * NW) void attn_decode_kernel(const AttnParams p
   const int h2 = lane >> 5;
   const int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
   const int nq = (int)p.n_q;
-  const bool computes = wave * 32 < p.G * nq;  // wave-uniform
+  const int pair = wave >> 1, half = wave & 1;      // wave-uniform
+  const bool computes = pair * 32 < p.G * nq;       // wave-uniform
 
-  const int rho = wave * 32 + l32;
+  const int rho = pair * 32 + l32;
   const bool valid = rho < p.G * nq;
   const int g = valid ? rho / nq : 0;
   const int hq = hkv * p.G + g;
@@ -729,13 +745,13 @@ __global__ __launch_bounds__(64 * NW) void attn_decode_kernel(const AttnParams p
     if (computes) {
       const uint16_t* ks = k_st[cur];
       const uint16_t* vs = v_st[cur];
-      f32x16 s_cur[2];
-      qk_tile<D>(ks, koff, qf, rows.qk_init(), s_cur);
-      rows.mask(p, s_cur, j0_of(t), h2);
+      f32x16 s_cur[1];
+      qk_tile<D, 1>(ks, koff, qf, rows.qk_init(), s_cur, half);
+      rows.mask(p, s_cur, j0_of(t), h2, half);
       rows.rescale(rows.tile_max(s_cur), s_cur);
-      u32x4 pf[4];
+      u32x4 pf[2];
       rows.probs(s_cur, pf);
-      pv_tile<D, VT>(vs, voff, pf, rows.oacc);
+      pv_tile<D, VT, 1>(vs, voff, pf, rows.oacc, half);
     }
     // tile t + 1 landed (the NST - 2 newer tiles may still be in flight)
     if (pre)
@@ -743,6 +759,36 @@ __global__ __launch_bounds__(64 * NW) void attn_decode_kernel(const AttnParams p
     else
       stage_barrier<0>();
     cur = cur == NST - 1 ? 0 : cur + 1;
+  }
+
+  // The second wave of each pair hands its state to the first through LDS:
+  // every copy has landed and every wave has passed the last barrier, so the
+  // stages are free.  Per lane: the O slice, m, l (XS floats).
+  constexpr int XS = (D / 32) * 16 + 2;
+  static_assert(NW / 2 * 64 * XS * 4 <= NST * T::ELEMS * 2, "exchange fits the K stages");
+  float* xbuf = reinterpret_cast<float*>(&k_st[0][0]) + (pair * 64 + lane) * XS;
+  if (computes && half == 1) {
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xbuf[i * 16 + r] = rows.oacc[i][r];
+    xbuf[XS - 2] = rows.m_run;
+    xbuf[XS - 1] = rows.l_run;
+  }
+  __syncthreads();
+  if (!computes || half == 1) return;
+  {
+    // merge by the two reference maxima (exact: O and l scale alike)
+    const float ma = rows.m_run, mb = xbuf[XS - 2];
+    const float m = fmaxf(ma, mb);
+    const float fa = (ma == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ma - m);
+    const float fb = (mb == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mb - m);
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) rows.oacc[i][r] = rows.oacc[i][r] * fa + xbuf[i * 16 + r] * fb;
+    rows.l_run = rows.l_run * fa + xbuf[XS - 1] * fb;
+    rows.m_run = m;
   }
 
   // this split's partial, fp32 [B][Hq][n_q][d] and [B][Hq][n_q]

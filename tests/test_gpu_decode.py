@@ -27,6 +27,7 @@ CASES = [
     ("d64_g4_q3", 4, 1, 64, 1000, 3, None, "pi", -1, 0, False, (2, 16)),
     ("d128_rows_mid", 8, 2, 128, 2000, 8, 100, "plain", -1, 0, True, (4,)),
     ("d64_g2_q8_pairs", 4, 2, 64, 700, 8, None, "pair_factors", 64, 2, True, (5,)),
+    ("d64_g8_q8_two_pairs", 8, 1, 64, 1300, 8, None, "ntk", -1, 0, True, (1, 9, 30)),
 ]
 
 
