@@ -66,11 +66,17 @@ __device__ __forceinline__ int b_swz(int r) {
 // land as zeros) and spans at most one tile, so any row stride below 2^25
 // elements keeps offsets in 32 bits.
 // Tiles of the 16-key dK/dV kernel: its transposing reads take 2 chunks of 8
-// consecutive rows per 32 lanes, so (c ^ s_swz(r)) >> 1 differs over 8
-// consecutive rows; its row reads still see 16 distinct slots over 16 rows.
+// consecutive rows per 32 lanes (a wave's two halves are served in separate
+// passes), so (c ^ s_swz(r)) >> 1 differs over 8 consecutive rows.  For its
+// row reads (ds_read_b128, 16 rows x 4 chunks per wave) the bit of row 8
+// enters slot bit 2, not bit 0 (D = 128): among the swizzles that keep the
+// transposing reads clean, these are the ones the hardware's bank-conflict
+// counter reads as zero for both read patterns (the counter gave 4 conflict
+// cycles per row read with bit 0, and with the first form for d = 64).
 template <int D>
 __device__ __forceinline__ int s_swz(int r) {
-  return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+  return D == 128 ? (((r & 7) << 1) ^ (((r >> 3) & 1) << 2))
+                  : ((((r >> 1) & 1) << 2) ^ (((r >> 2) & 1) << 1) ^ (((r >> 3) & 1) << 2));
 }
 
 template <int D, bool S16>
