@@ -28,7 +28,8 @@
 //  * Q is rotated (RoPE from the fp32 tables) once per workgroup in registers;
 //    K is either pre-rotated (f16) or rotated while being staged.
 //  * Rotated q/k are rounded once to f16 (three more mantissa bits than bf16:
-//    it keeps the LSE of short rows within 1e-3), P to bf16.
+//    it keeps the LSE of short rows within 1e-3); P to f16 against V tiles,
+//    to bf16 against V rows.
 //  * Online softmax in base 2: Q is scaled by sigma·log2(e) before its f16
 //    rounding and the QK^T product starts from -m (the row's reference max)
 //    in the accumulator, so the scores come out ready for exp2 with no
