@@ -103,6 +103,17 @@ def traffic_from_profile(launch_flop_bytes):
     return rec.get("hbm_bytes_per_launch")
 
 
+def kv_cache_bytes_per_token(n_layers: int, n_kv_heads: int, head_dim: int, dtype_bytes: int = 2) -> int:
+    """KV cache per token: K and V of every layer and KV head."""
+    return 2 * n_layers * n_kv_heads * head_dim * dtype_bytes
+
+
+def backward_flop(w) -> float:
+    """Algorithmic FLOP of the backward pass: five products (S, dP, dV, dK, dQ)
+    of 2·d FLOP per kept pair per query head, i.e. 2.5 times the forward's."""
+    return 2.5 * w.flop()
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -314,7 +325,8 @@ def bench_decode(args, w):
     ms = float(np.median([e[0].elapsed_time(e[2]) for e in evs]))
     tab_ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
     dec_ms = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
-    cache_bytes = w.B * w.Hkv * w.n * w.d * 2 + w.B * w.Hkv * 64 * ((w.n + 63) // 64) * w.d * 2
+    # one layer's cache: K rows (f16) and V tiles (f16, the last tile padded to 64 keys)
+    cache_bytes = w.B * (w.n + 64 * ((w.n + 63) // 64)) * kv_cache_bytes_per_token(1, w.Hkv, w.d) // 2
     io_bytes = w.B * w.Hq * n_q * w.d * (2 + 2) + 2 * n_splits * w.B * w.Hq * n_q * (w.d + 1) * 4
     gbs = (cache_bytes + io_bytes) / (ms * 1e-3) / 1e9
     dec_gbs = (cache_bytes + io_bytes) / (dec_ms * 1e-3) / 1e9
@@ -354,13 +366,13 @@ def cpu_baseline_bwd(w, m: int):
         t0 = time.perf_counter()
         oracle.attn_bwd(q[:, :, :mm], k[:, :, :mm], v[:, :, :mm], g[:, :, :mm], th, pf, lm / np.sqrt(w.d),
                         True, w.window, w.n_sink)
-        return 2.5 * w.with_(n=mm).flop(), time.perf_counter() - t0
+        return backward_flop(w.with_(n=mm)), time.perf_counter() - t0
 
     flop, dt = run(m)
     one = _single_core(lambda: run(max(1, m // 4)), 1.0)
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle", "seconds": round(dt, 3), "cpu_model": cpu_model(),
-            "single_core_value": one, "extrapolated_full_layer_s": round(2.5 * w.flop() / (flop / dt), 1),
+            "single_core_value": one, "extrapolated_full_layer_s": round(backward_flop(w) / (flop / dt), 1),
             "sample": f"the first {m} positions of all {w.Hq} query heads of the same layer (dq, dk, dv "
                       f"in full), fp64, {flop:.3e} algorithmic FLOP (5 products per kept pair); single "
                       f"core on the first {max(1, m // 4)} positions"}
@@ -415,7 +427,7 @@ def bench_backward(args, w):
     wall = time.perf_counter() - t0
     bwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     ms_step = wall * 1e3 / args.steps
-    flop = 2.5 * w.flop()   # S, dP, dV, dK, dQ: five products per kept pair
+    flop = backward_flop(w)   # S, dP, dV, dK, dQ: five products per kept pair
     value = flop / (ms_step * 1e-3) / 1e12
     ach = flop / (bwd_ms * 1e-3) / 1e12
     out = {
