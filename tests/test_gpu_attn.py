@@ -338,3 +338,41 @@ def test_accumulate_two_halves_equals_one_shot(lcx):
     d_o = (o - o_ref).abs()
     assert d_o.max().item() < U.O_MAX_ABS and d_o.mean().item() < 1e-4
     assert (l - l_ref).abs().max().item() < 5e-5
+
+
+def test_chunks_merged_in_any_order(lcx):
+    # a ring rank receives the key chunks in rotated order: every order of the
+    # fused-merge calls gives the one-shot result and the oracle's (chunks of
+    # 192 keys, not tile aligned, over a window + sink mask and tiled V)
+    w = W.TINY.with_(Hq=4, Hkv=2, d=128, base=500000.0, n=1100, seed=21, window=300, n_sink=3)
+    q, k, v = U.inputs(w)
+    qd, kd, vd = U.to_dev(q), U.to_dev(k), U.to_dev(v)
+    cfg = _cfg(lcx, w)
+    cos, sin = lcx.rope_tables(cfg, w.n, device=U.dev())
+    _, kr = lcx.rope_apply_qk(None, kd, cos, sin)
+    o1, l1 = lcx.attn_fwd(qd, kr, lcx.pack_v(vd), rope_q=True, cos=cos, sin=sin, rope=cfg, window=w.window,
+                          n_sink=w.n_sink, out_dtype=torch.float32)
+    bounds = list(range(0, w.n, 192)) + [w.n]
+    chunks = [(bounds[c], bounds[c + 1]) for c in range(len(bounds) - 1)]
+    orders = [list(range(len(chunks))), list(reversed(range(len(chunks)))),
+              [int(c) for c in np.random.default_rng(5).permutation(len(chunks))]]
+    outs = []
+    for order in orders:
+        o = torch.zeros((1, w.Hq, w.n, w.d), dtype=torch.float32, device=U.dev())
+        l = torch.full((1, w.Hq, w.n), float("-inf"), dtype=torch.float32, device=U.dev())
+        for c in order:
+            a, b = chunks[c]
+            vt = lcx.pack_v(vd[:, :, a:b].contiguous())
+            lcx.attn_fwd(qd, kr[:, :, a:b], vt, o, l, rope_q=True, cos=cos, sin=sin, rope=cfg,
+                         window=w.window, n_sink=w.n_sink, k_pos0=a, accumulate=True)
+        torch.cuda.synchronize()
+        outs.append((o, l))
+    bb, hh, rr = U.sample_rows(w, 600, seed=3)
+    o_ref, l_ref = U.oracle_rows(w, q, k, v, bb, hh, rr)
+    for (o, l), order in zip(outs, orders):
+        d_o = (o - o1).abs()
+        assert d_o.max().item() < U.O_MAX_ABS and d_o.mean().item() < 1e-4, order
+        # each side's row sums round P to f16 against its own reference max:
+        # at most 2^-12 relative for these short window rows, so 2 x 2^-12 apart
+        assert (l - l1).abs().max().item() < 5e-4, order
+        U.check(o.cpu().numpy()[bb, hh, rr], l.cpu().numpy()[bb, hh, rr], o_ref, l_ref, f"order {order[:3]}")
