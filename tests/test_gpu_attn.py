@@ -376,3 +376,37 @@ def test_chunks_merged_in_any_order(lcx):
         # at most 2^-12 relative for these short window rows, so 2 x 2^-12 apart
         assert (l - l1).abs().max().item() < 5e-4, order
         U.check(o.cpu().numpy()[bb, hh, rr], l.cpu().numpy()[bb, hh, rr], o_ref, l_ref, f"order {order[:3]}")
+
+
+@pytest.mark.parametrize("v_tiled", [False, True], ids=["v_rows", "v_tiles"])
+def test_prerotated_queries(lcx, v_tiled):
+    # q rotated beforehand (lcx_rope_apply_qk): the kernel only scales it by
+    # sigma·log2 e on load; YaRN's temperature reaches the scale through the
+    # rope configuration.  f16 q and k against the exact oracle; bf16 q and k
+    # against the oracle on the same rounded rotated values (a bf16 rotated q
+    # alone moves short rows' LSE by ~2e-3, which is why the kernel rotates
+    # into f16)
+    w = W.TINY.with_(Hq=8, Hkv=2, d=128, base=500000.0, n=700, seed=31, scheme="yarn", L_train=128,
+                     L_target=512)
+    q, k, v = U.inputs(w)
+    qd, kd, vd = U.to_dev(q), U.to_dev(k), U.to_dev(v)
+    cfg = _cfg(lcx, w)
+    cos, sin = lcx.rope_tables(cfg, w.n, device=U.dev())
+    vv = lcx.pack_v(vd) if v_tiled else vd
+    layout = "tiles" if v_tiled else "rows"
+    o_ref, l_ref = _all(w, q, k, v)
+    qr, kr = lcx.rope_apply_qk(qd, kd, cos, sin, out_dtype=torch.float16)
+    o, lse = lcx.attn_fwd(qr, kr, vv, rope=cfg)
+    torch.cuda.synchronize()
+    U.check(o.float().cpu().numpy().reshape(-1, w.d), lse.cpu().numpy().reshape(-1), o_ref, l_ref,
+            f"prerotated q f16/{layout}")
+    qb, kb = lcx.rope_apply_qk(qd, kd, cos, sin, out_dtype=torch.bfloat16)
+    o, lse = lcx.attn_fwd(qb, kb, vv, rope=cfg)
+    torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+    B, Hq, n, d = q.shape
+    bb, hh, rr = np.meshgrid(np.arange(B), np.arange(Hq), np.arange(n), indexing="ij")
+    o_rb, l_rb = U.oracle_rows(w, bits(qb), bits(kb), v, bb.reshape(-1).astype(np.int32),
+                               hh.reshape(-1).astype(np.int32), rr.reshape(-1), rope=False)
+    U.check(o.float().cpu().numpy().reshape(-1, w.d), lse.cpu().numpy().reshape(-1), o_rb, l_rb,
+            f"prerotated q bf16/{layout}")
