@@ -372,8 +372,9 @@ def test_chunks_merged_in_any_order(lcx):
     for (o, l), order in zip(outs, orders):
         d_o = (o - o1).abs()
         assert d_o.max().item() < U.O_MAX_ABS and d_o.mean().item() < 1e-4, order
-        # each side's row sums round P to f16 against its own reference max:
-        # at most 2^-12 relative for these short window rows, so 2 x 2^-12 apart
+        # each side's row sums round P to f16 (2^-11 relative at most) against
+        # its own reference max: independent roundings over rows of >= 193
+        # keys, far inside the worst case of 2 x 2^-11
         assert (l - l1).abs().max().item() < 5e-4, order
         U.check(o.cpu().numpy()[bb, hh, rr], l.cpu().numpy()[bb, hh, rr], o_ref, l_ref, f"order {order[:3]}")
 
@@ -410,3 +411,46 @@ def test_prerotated_queries(lcx, v_tiled):
                                hh.reshape(-1).astype(np.int32), rr.reshape(-1), rope=False)
     U.check(o.float().cpu().numpy().reshape(-1, w.d), lse.cpu().numpy().reshape(-1), o_rb, l_rb,
             f"prerotated q bf16/{layout}")
+
+
+def test_chunked_driver_with_window_and_sinks(lcx):
+    # lcx_attn_fwd_chunked over a window + sink mask: chunks that lie wholly
+    # outside a row's window contribute nothing, the sink chunk always does;
+    # 3000 keys in chunks of 448 leave a ragged last chunk of 312
+    # chunk length 448 leaves a ragged last chunk
+    w = W.MILLION.with_(n=3000, chunk=448, Hq=8, Hkv=2, seed=23, window=700, n_sink=4, scheme="pi")
+    q, k, v = U.inputs(w)
+    qd, kd, vd = U.to_dev(q), U.to_dev(k), U.to_dev(v)
+    cfg = _cfg(lcx, w)
+    cos, sin = lcx.rope_tables(cfg, w.n, device=U.dev())
+    _, kr = lcx.rope_apply_qk(None, kd, cos, sin)
+    vt = lcx.pack_v(vd)
+    acc_o = torch.empty((1, w.Hq, w.n, w.d), dtype=torch.float32, device=U.dev())
+    acc_l = torch.empty((1, w.Hq, w.n), dtype=torch.float32, device=U.dev())
+    o, lse = lcx.attn_fwd_chunked(qd, kr, vd, w.chunk, acc_o, acc_l, rope_q=True, cos=cos, sin=sin,
+                                  rope=cfg, window=w.window, n_sink=w.n_sink)
+    torch.cuda.synchronize()
+    bb, hh, rr = U.sample_rows(w, 1500)
+    o_ref, l_ref = U.oracle_rows(w, q, k, v, bb, hh, rr)
+    U.check(o.float().cpu().numpy()[bb, hh, rr], lse.cpu().numpy()[bb, hh, rr], o_ref, l_ref,
+            "chunked window+sinks")
+    o1, l1 = lcx.attn_fwd(qd, kr, vd, rope_q=True, cos=cos, sin=sin, rope=cfg, window=w.window,
+                          n_sink=w.n_sink, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    d_o = (acc_o - o1).abs()
+    assert d_o.max().item() < U.O_MAX_ABS and d_o.mean().item() < 1e-4
+    # rows past the first chunk keep >= 449 keys; both sides round P to f16
+    # against their own reference max, independently (worst case 2 x 2^-11)
+    assert (acc_l - l1).abs().max().item() < 2.5e-4
+    # the same chunks over tiled V: LSE bit-identical, O within rounding
+    acc_o2, acc_l2 = torch.empty_like(acc_o), torch.empty_like(acc_l)
+    lcx.attn_fwd_chunked(qd, kr, vt, w.chunk, acc_o2, acc_l2, rope_q=True, cos=cos, sin=sin,
+                         rope=cfg, window=w.window, n_sink=w.n_sink)
+    torch.cuda.synchronize()
+    assert torch.equal(acc_l2, acc_l)
+    d_o2 = (acc_o2 - acc_o).abs()
+    assert d_o2.max().item() < U.O_MAX_ABS and d_o2.mean().item() < 1e-4
+    # a chunk that is not a multiple of 64 cannot start on a V tile: rejected
+    with pytest.raises(lcx.LcxError):
+        lcx.attn_fwd_chunked(qd, kr, vt, 300, acc_o2, acc_l2, rope_q=True, cos=cos, sin=sin,
+                             rope=cfg, window=w.window, n_sink=w.n_sink)

@@ -69,3 +69,26 @@ def test_decode_rows_before_the_cache_are_empty(lcx):
                              rope=cfg, q_pos0=10, k_pos0=600)
     torch.cuda.synchronize()
     assert torch.isneginf(lse).all().item() and (o.float() == 0).all().item()
+
+
+def test_decode_two_batches(lcx):
+    # batch index on the grid's third axis: two caches of different content,
+    # 3 new rows each, every row compared
+    w = W.Workload("decode_b2", 2, 8, 2, 128, 1500, "yarn", 500000.0, 256, 1024, cur_len=1500, seed=41)
+    n_q = 3
+    q, _, _ = U.inputs(w, n_q=n_q)
+    _, k, v = U.inputs(w)
+    cfg = lcx.rope_cfg(w.scheme, w.base, w.d, w.L_train, w.L_target, w.cur_len, w.alpha, w.beta)
+    cos, sin = lcx.rope_tables(cfg, w.n, device=U.dev())
+    qd, kd, vd = U.to_dev(q), U.to_dev(k), U.to_dev(v)
+    _, kr = lcx.rope_apply_qk(None, kd, cos, sin)
+    qp0 = w.n - n_q
+    bb, hh, rr = np.meshgrid(np.arange(w.B), np.arange(w.Hq), np.arange(n_q), indexing="ij")
+    bb, hh, rr = bb.reshape(-1).astype(np.int32), hh.reshape(-1).astype(np.int32), rr.reshape(-1)
+    o_ref, l_ref = U.oracle_rows(w, q, k, v, bb, hh, rr, q_pos0=qp0)
+    for vv, ns in ((lcx.pack_v(vd), 6), (vd, 11)):
+        o, lse = lcx.attn_decode(qd, kr, vv, n_splits=ns, rope_q=True, cos=cos, sin=sin, rope=cfg,
+                                 q_pos0=qp0, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        U.check(o.cpu().numpy().reshape(-1, w.d), lse.cpu().numpy().reshape(-1), o_ref, l_ref,
+                f"decode/B=2/splits={ns}")
