@@ -417,7 +417,6 @@ def test_chunked_driver_with_window_and_sinks(lcx):
     # lcx_attn_fwd_chunked over a window + sink mask: chunks that lie wholly
     # outside a row's window contribute nothing, the sink chunk always does;
     # 3000 keys in chunks of 448 leave a ragged last chunk of 312
-    # chunk length 448 leaves a ragged last chunk
     w = W.MILLION.with_(n=3000, chunk=448, Hq=8, Hkv=2, seed=23, window=700, n_sink=4, scheme="pi")
     q, k, v = U.inputs(w)
     qd, kd, vd = U.to_dev(q), U.to_dev(k), U.to_dev(v)
