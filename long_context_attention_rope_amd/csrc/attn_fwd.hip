@@ -325,6 +325,24 @@ struct Rows32 {
   float l_run;  // this lane's partial row sum
   int64_t qi;   // this lane's row
   int64_t qpos, qpos_min, qpos_max;
+  // a tile starting at key j0 is kept whole for every row of the group iff
+  // j0 <= kt_hi and (j0 >= kt_lo or j0 < kt_sink): the 64-bit position tests
+  // done once, so that each tile decides with 32-bit scalar compares
+  int kt_hi, kt_lo, kt_sink;
+
+  __device__ __forceinline__ static int sat_i32(int64_t x) {
+    return (int)(x > INT32_MAX ? (int64_t)INT32_MAX : (x < INT32_MIN ? (int64_t)INT32_MIN : x));
+  }
+  __device__ __forceinline__ void set_kept_tiles(const AttnParams& p) {
+    // j0 + BN <= n_kv; causal: k_pos0 + j0 + BN - 1 <= qpos_min
+    int64_t hi = p.n_kv - BN;
+    if (p.causal) hi = hi < qpos_min - p.k_pos0 - (BN - 1) ? hi : qpos_min - p.k_pos0 - (BN - 1);
+    kt_hi = sat_i32(hi);
+    // window: k_pos0 + j0 >= qpos_max - window, or every key a sink:
+    // k_pos0 + j0 + BN - 1 < n_sink
+    kt_lo = p.window >= 0 ? sat_i32(qpos_max - p.window - p.k_pos0) : INT32_MIN;
+    kt_sink = sat_i32((int64_t)p.n_sink - p.k_pos0 - (BN - 1));
+  }
 
   __device__ __forceinline__ void init(const AttnParams& p, int64_t row0, int l32) {
 #pragma unroll
@@ -340,6 +358,7 @@ struct Rows32 {
     const int64_t last = (row0 + 31 < p.n_q ? row0 + 31 : p.n_q - 1);
     qpos_min = p.q_pos0 + row0;
     qpos_max = p.q_pos0 + (last >= row0 ? last : row0);
+    set_kept_tiles(p);
   }
   // lane row qi (>= n_q: no row) of a group whose kept positions span
   // [qpos_lo, qpos_hi]
@@ -357,31 +376,33 @@ struct Rows32 {
     qpos = p.q_pos0 + row;
     qpos_min = qpos_lo;
     qpos_max = qpos_hi;
+    set_kept_tiles(p);
   }
   // mask S(t), blocks kb0 .. kb0 + NB - 1 (only for tiles that straddle a
   // mask edge for these rows)
   template <int NB>
   __device__ __forceinline__ void mask(const AttnParams& p, f32x16 (&s)[NB], int j0, int h2, int kb0 = 0) const {
-    const int64_t kpos_min = p.k_pos0 + j0;
-    const int64_t kpos_max = p.k_pos0 + (j0 + BN <= p.n_kv ? j0 + BN : p.n_kv) - 1;
-    const bool all_kept = (j0 + BN <= p.n_kv) && (!p.causal || kpos_max <= qpos_min) &&
-                          (p.window < 0 || kpos_min >= qpos_max - p.window ||
-                           kpos_max < (int64_t)p.n_sink);
-    if (!all_kept) {
+    if (!(j0 <= kt_hi && (j0 >= kt_lo || j0 < kt_sink))) {
+      const int64_t kpos_min = p.k_pos0 + j0;
       // Branch-free, in 32-bit offsets within the tile: key at offset `off`
       // (position kpos_min + off) is kept iff off < krem (exists),
       // off <= hi (causal), and off >= lo (window) or off < srem (sink).
+      // off = bias + c with c a constant of the unrolled loop, so every bound
+      // is moved by bias once and each element compares against c (an
+      // inline constant, no per-element offset registers)
       const int64_t rel = qpos - kpos_min;
       const int hi = p.causal ? clamp_i32(rel) : (1 << 30);
       const int lo = p.window >= 0 ? clamp_i32(rel - p.window) : -(1 << 30);
       const int srem = clamp_tile((int64_t)p.n_sink - kpos_min);
       const int krem = clamp_tile(p.n_kv - j0);
+      const int bias = kb0 * 32 + h2 * 4;
+      const int a_k = krem - bias, a_hi = hi - bias, a_lo = lo - bias, a_s = srem - bias;
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int off = (kb0 + kb) * 32 + (r >> 2) * 8 + h2 * 4 + (r & 3);
-          const bool ok = (off < krem) & (off <= hi) & ((off >= lo) | (off < srem));
+          const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
+          const bool ok = (c < a_k) & (c <= a_hi) & ((c >= a_lo) | (c < a_s));
           s[kb][r] = ok ? s[kb][r] : -INFINITY;
         }
     }
