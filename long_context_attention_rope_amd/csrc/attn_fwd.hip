@@ -255,6 +255,21 @@ struct KRegStage {
 // (n, h2) reads chunk 2c + h2 of K row 32(kb0 + kb) + n (koff[c] holds that
 // row-in-block and swizzled chunk); the products accumulate onto `init` (-m
 // of the lane's row).
+// Scheduling constraint for a run of N (LDS operand read, MFMA) pairs: the
+// first AHEAD reads, then one product and one read alternately, then the last
+// AHEAD products, so that AHEAD reads are in flight while products issue.
+template <int N, int AHEAD, int ID>
+__device__ __forceinline__ void pipeline_reads() {
+  constexpr int AH = N > AHEAD ? AHEAD : N;
+  __builtin_amdgcn_sched_group_barrier(0x100, AH, ID);  // LDS reads
+#pragma unroll
+  for (int i = 0; i < N - AH; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, ID);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AH, ID);
+}
+
 template <int D, int NB = 2>
 __device__ __forceinline__ void qk_tile(const uint16_t* ks, const int (&koff)[D / 16],
                                         const f16x8 (&qf)[D / 16], const f32x16& init,
@@ -267,6 +282,9 @@ __device__ __forceinline__ void qk_tile(const uint16_t* ks, const int (&koff)[D 
       s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[c], c == 0 ? init : s[kb], 0, 0, 0);
     }
   }
+  // keep four operand reads in flight ahead of the products (left to
+  // itself the scheduler issues each read one product ahead and waits on it)
+  pipeline_reads<(D / 16) * NB, 4, 0>();
 }
 
 // A operand of O^T += V^T·P^T for d-block db and 16-key chunk kc.  Lane l
@@ -297,10 +315,11 @@ __device__ __forceinline__ u32x4 pv_operand(const uint16_t* vt, const int (&voff
 template <int D, bool VT, int NB = 2>
 __device__ __forceinline__ void pv_tile(const uint16_t* vs, const int (&voff)[4], const u32x4 (&pf)[2 * NB],
                                         f32x16 (&oacc)[D / 32], int kb0 = 0) {
+  // key chunk outer: consecutive products go to different accumulators
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int kc = 0; kc < 2 * NB; ++kc)
 #pragma unroll
-    for (int kc = 0; kc < 2 * NB; ++kc) {
+    for (int db = 0; db < D / 32; ++db) {
       const u32x4 a = pv_operand<D, VT>(vs, voff, db, 2 * kb0 + kc);
       if constexpr (VT)
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
@@ -309,6 +328,7 @@ __device__ __forceinline__ void pv_tile(const uint16_t* vs, const int (&voff)[4]
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                            __builtin_bit_cast(bf16x8, pf[kc]), oacc[db], 0, 0, 0);
     }
+  pipeline_reads<(D / 32) * 2 * NB, 4, 1>();
 }
 
 // Online-softmax state and O accumulator of 32 query rows of one head.  Row n
