@@ -255,21 +255,6 @@ struct KRegStage {
 // (n, h2) reads chunk 2c + h2 of K row 32(kb0 + kb) + n (koff[c] holds that
 // row-in-block and swizzled chunk); the products accumulate onto `init` (-m
 // of the lane's row).
-// Scheduling constraint for a run of N (LDS operand read, MFMA) pairs: the
-// first AHEAD reads, then one product and one read alternately, then the last
-// AHEAD products, so that AHEAD reads are in flight while products issue.
-template <int N, int AHEAD, int ID>
-__device__ __forceinline__ void pipeline_reads() {
-  constexpr int AH = N > AHEAD ? AHEAD : N;
-  __builtin_amdgcn_sched_group_barrier(0x100, AH, ID);  // LDS reads
-#pragma unroll
-  for (int i = 0; i < N - AH; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, ID);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, AH, ID);
-}
-
 template <int D, int NB = 2>
 __device__ __forceinline__ void qk_tile(const uint16_t* ks, const int (&koff)[D / 16],
                                         const f16x8 (&qf)[D / 16], const f32x16& init,
@@ -284,7 +269,7 @@ __device__ __forceinline__ void qk_tile(const uint16_t* ks, const int (&koff)[D 
   }
   // keep four operand reads in flight ahead of the products (left to
   // itself the scheduler issues each read one product ahead and waits on it)
-  pipeline_reads<(D / 16) * NB, 4, 0>();
+  pipeline_reads<(D / 16) * NB, 1, 4, 0>();
 }
 
 // A operand of O^T += V^T·P^T for d-block db and 16-key chunk kc.  Lane l
@@ -328,7 +313,7 @@ __device__ __forceinline__ void pv_tile(const uint16_t* vs, const int (&voff)[4]
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                            __builtin_bit_cast(bf16x8, pf[kc]), oacc[db], 0, 0, 0);
     }
-  pipeline_reads<(D / 32) * 2 * NB, 4, 1>();
+  pipeline_reads<(D / 32) * 2 * NB, 1, 4, 1>();
 }
 
 // Online-softmax state and O accumulator of 32 query rows of one head.  Row n

@@ -44,6 +44,25 @@ __device__ __forceinline__ int clamp_tile(int64_t x) {
   return (int)(x < 0 ? 0 : (x > BN ? BN : x));
 }
 
+// Scheduling constraint for a run of N MFMAs, each fed by R LDS operand reads
+// of the same basic block: the reads of the first AHEAD products, then one
+// product and the reads of a later one alternately, then the last AHEAD
+// products, so that AHEAD products' reads are in flight while products issue
+// (left to itself the scheduler issues each read one product ahead and waits
+// on it).  Only the order changes; the waits are still inserted by the
+// compiler.
+template <int N, int R, int AHEAD, int ID>
+__device__ __forceinline__ void pipeline_reads() {
+  constexpr int AH = N > AHEAD ? AHEAD : N;
+  __builtin_amdgcn_sched_group_barrier(0x100, AH * R, ID);  // LDS reads
+#pragma unroll
+  for (int i = 0; i < N - AH; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, R, ID);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AH, ID);
+}
+
 // Buffer resource over [base, base + bytes): lane offsets >= bytes read zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
