@@ -269,25 +269,48 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(const BwdParams p) {
 
 // ---------------------------------------------------------------- dq
 
+// Tile starts j0 whose 64 keys every row of a wave (positions [qpos_min,
+// qpos_max]) keeps: j0 <= hi and (j0 >= lo or j0 < sink).  The 64-bit
+// position tests run once per wave, saturated to the int32 range (which keeps
+// every outcome for tile starts in [0, 2^31 - 1)), so that each tile decides
+// with 32-bit scalar compares.
+struct KeptTiles {
+  int hi, lo, sink;
+  __device__ __forceinline__ static int sat(int64_t x) {
+    return (int)(x > INT32_MAX ? (int64_t)INT32_MAX : (x < INT32_MIN ? (int64_t)INT32_MIN : x));
+  }
+  __device__ __forceinline__ void init(const BwdParams& p, int64_t qpos_min, int64_t qpos_max) {
+    // j0 + BN <= n_kv; causal: k_pos0 + j0 + BN - 1 <= qpos_min
+    int64_t h = p.n_kv - BN;
+    if (p.causal) h = h < qpos_min - p.k_pos0 - (BN - 1) ? h : qpos_min - p.k_pos0 - (BN - 1);
+    hi = sat(h);
+    // window: k_pos0 + j0 >= qpos_max - window, or every key a sink
+    lo = p.window >= 0 ? sat(qpos_max - p.window - p.k_pos0) : INT32_MIN;
+    sink = sat((int64_t)p.n_sink - p.k_pos0 - (BN - 1));
+  }
+  __device__ __forceinline__ bool whole(int j0) const { return j0 <= hi && (j0 >= lo || j0 < sink); }
+};
+
 // Key mask of half kb of a 64-key tile for the lane's query row (S^T
 // accumulator layout: register r is key kb·32 + (r/4)·8 + 4h + r%4); tiles
-// that every row of the wave keeps whole are left alone.
-__device__ __forceinline__ void mask_keys(const BwdParams& p, f32x16& s, int64_t j0, int kb, int64_t qpos,
-                                          int64_t qpos_min, int64_t qpos_max, int h) {
+// that every row of the wave keeps whole are left alone.  The lane's key
+// offset is bias + c with c a constant of the unrolled loop: the bounds are
+// shifted by bias once and each element compares against an inline constant.
+__device__ __forceinline__ void mask_keys(const BwdParams& p, f32x16& s, int j0, int kb, int64_t qpos,
+                                          const KeptTiles& kt, int h) {
+  if (kt.whole(j0)) return;
   const int64_t kpos_min = p.k_pos0 + j0;
-  const int64_t kpos_max = p.k_pos0 + (j0 + BN <= p.n_kv ? j0 + BN : p.n_kv) - 1;
-  const bool all_kept = (j0 + BN <= p.n_kv) && (!p.causal || kpos_max <= qpos_min) &&
-                        (p.window < 0 || kpos_min >= qpos_max - p.window || kpos_max < (int64_t)p.n_sink);
-  if (all_kept) return;
   const int64_t rel = qpos - kpos_min;
   const int hi = p.causal ? clamp_i32(rel) : (1 << 30);
   const int lo = p.window >= 0 ? clamp_i32(rel - p.window) : -(1 << 30);
   const int srem = clamp_tile((int64_t)p.n_sink - kpos_min);
   const int krem = clamp_tile(p.n_kv - j0);
+  const int bias = kb * 32 + h * 4;
+  const int a_k = krem - bias, a_hi = hi - bias, a_lo = lo - bias, a_s = srem - bias;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int off = kb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-    const bool ok = (off < krem) & (off <= hi) & ((off >= lo) | (off < srem));
+    const int c = (r >> 2) * 8 + (r & 3);
+    const bool ok = (c < a_k) & (c <= a_hi) & ((c >= a_lo) | (c < a_s));
     s[r] = ok ? s[r] : -INFINITY;
   }
 }
@@ -313,6 +336,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(const BwdParams
   const int64_t wlast = (bt.row0 + 32 * wave + 31 < p.n_q ? bt.row0 + 32 * wave + 31 : p.n_q - 1);
   const int64_t qpos_min = p.q_pos0 + bt.row0 + 32 * wave;
   const int64_t qpos_max = p.q_pos0 + (wlast >= bt.row0 + 32 * wave ? wlast : bt.row0 + 32 * wave);
+  KeptTiles kt;
+  kt.init(p, qpos_min, qpos_max);
 
   bf16x8 qf[D / 16], gf[D / 16];
   load_frag<D>(p.q + bt.b * p.qs_b + bt.hq * p.qs_h, qi, qvalid, p.qs_s, h, qf);
@@ -359,7 +384,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(const BwdParams
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(to.row_op(ks, kb, c), qf[c], sc, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(to.row_op(vs, kb, c), gf[c], dp, 0, 0, 0);
       }
-      mask_keys(p, sc, j0, kb, qpos, qpos_min, qpos_max, h);
+      mask_keys(p, sc, j0, kb, qpos, kt, h);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], p.scale_log2, -lse2));
@@ -508,6 +533,21 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
   const bool keys_whole = wkey0 + 16 <= p.n_kv;
   const int64_t wkpos_min = p.k_pos0 + wkey0, wkpos_max = wkpos_min + 15;
   const bool k_sink = kpos < (int64_t)p.n_sink;
+  // row tiles (first row at query position q_pos0 + j0) whose 64 rows all
+  // keep the wave's 16 keys: rt_lo <= j0 <= rt_hi, with the keys whole; the
+  // 64-bit tests once per wave (saturated to int32, which keeps every outcome
+  // for j0 in [0, 2^31 - 1)), 32-bit scalar compares per step
+  int rt_lo, rt_hi;
+  {
+    int64_t h = p.n_q - BN;  // j0 + BN <= n_q
+    if (p.window >= 0 && !(wkpos_max < (int64_t)p.n_sink)) {
+      // q_pos0 + j0 + BN - 1 - window <= wkpos_min
+      const int64_t w = wkpos_min + p.window - p.q_pos0 - (BN - 1);
+      h = h < w ? h : w;
+    }
+    rt_hi = KeptTiles::sat(h);
+    rt_lo = p.causal ? KeptTiles::sat(wkpos_max - p.q_pos0) : INT32_MIN;  // q_pos0 + j0 >= wkpos_max
+  }
 
   // per-lane LDS offsets: row reads and the first transposing read
   int roff[D / 32], toff[D / 16];
@@ -542,9 +582,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
     if (pre) issue(qs_n, gs_n, ss_n, s + 2);
     const int64_t j0 = step_rows(s);
     const int64_t qpos_t = p.q_pos0 + j0;
-    const bool all_kept = keys_whole && (j0 + BN <= p.n_q) && (!p.causal || qpos_t >= wkpos_max) &&
-                          (p.window < 0 || qpos_t + BN - 1 - p.window <= wkpos_min ||
-                           wkpos_max < (int64_t)p.n_sink);
+    const bool all_kept = keys_whole && (int)j0 >= rt_lo && (int)j0 <= rt_hi;
     const int hi = clamp_i32(qpos_t - kpos);  // causal: row off kept iff hi + off >= 0
     const int lo = p.window >= 0 ? clamp_i32(qpos_t - kpos - p.window) : -(1 << 30);  // lo + off <= 0
     const int rrem = clamp_tile(p.n_q - j0);
