@@ -479,8 +479,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              f"(the path would shard by KV head group or by sequence ring, see the design notes).",
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the path would shard by KV head group, or by sequence as a ring of KV chunks).",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
