@@ -142,10 +142,11 @@ struct LdsCopy {
   }
   __device__ __forceinline__ void issue(uint16_t* lds, int j0) const {
     const uint32_t rows = n_kv > j0 ? (uint32_t)(n_kv - j0) : 0u;  // tiles past the end: empty range
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + j0 * rs, rows * (uint32_t)(rs * 2));
+    const uint32_t rs2 = (uint32_t)(rs * 2);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(reinterpret_cast<const char*>(base) + (uint64_t)(uint32_t)j0 * rs2, rows * rs2);
 #pragma unroll
     for (int i = 0; i < T::LPW; ++i) {
-      const uint32_t la = (uint32_t)(uintptr_t)(lds_void*)(lds + (row0 + i * T::RPL) * D);
+      const uint32_t la = (uint32_t)(uintptr_t)(lds_void*)lds + (uint32_t)((row0 + i * T::RPL) * D * 2);
       lds_copy16(r, off[i], __builtin_amdgcn_readfirstlane(la));
     }
   }
@@ -179,7 +180,7 @@ struct LdsCopyVT {
     const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (int64_t)(j0 / BN) * (D * BN), D * BN * 2);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      const uint32_t la = (uint32_t)(uintptr_t)(lds_void*)(lds + (row0 + i * 8) * BN);
+      const uint32_t la = (uint32_t)(uintptr_t)(lds_void*)lds + (uint32_t)((row0 + i * 8) * BN * 2);
       lds_copy16(r, off[i], __builtin_amdgcn_readfirstlane(la));
     }
   }
@@ -225,7 +226,8 @@ struct KRegStage {
   }
   __device__ __forceinline__ void load(int j0) {
     const uint32_t rows = n_kv > j0 ? (uint32_t)(n_kv - j0) : 0u;  // tiles past the end: empty range
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + j0 * rs, rows * (uint32_t)(rs * 2));
+    const uint32_t rs2 = (uint32_t)(rs * 2);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(reinterpret_cast<const char*>(base) + (uint64_t)(uint32_t)j0 * rs2, rows * rs2);
 #pragma unroll
     for (int i = 0; i < T::KCH; ++i) reg[i] = __builtin_amdgcn_raw_buffer_load_b128(r, off[i], 0, 0);
     if constexpr (KMODE == 2) {
@@ -327,6 +329,7 @@ struct Rows32 {
   f32x16 oacc[D / 32];
   f32x16 neg_m;  // -m_use in every element (KEEP_NEG_M)
   float m_run;  // reference max, log2 units (scaled); -inf before any kept key
+  float m_thr;  // a tile max (relative to m_use) above this moves m_run: kLazyTau, or -inf before any kept key
   float l_run;  // this lane's partial row sum
   int64_t qi;   // this lane's row
   int64_t qpos, qpos_min, qpos_max;
@@ -355,6 +358,7 @@ struct Rows32 {
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
     m_run = -INFINITY;
+    m_thr = -INFINITY;
     l_run = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) neg_m[r] = 0.f;
@@ -374,6 +378,7 @@ struct Rows32 {
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
     m_run = -INFINITY;
+    m_thr = -INFINITY;
     l_run = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) neg_m[r] = 0.f;
@@ -436,12 +441,14 @@ struct Rows32 {
     return xor32_max(mx);
   }
   // move the reference max when a row max grew by more than 2^kLazyTau, and
-  // shift this tile's s to the new reference
+  // shift this tile's s to the new reference.  The tile max mx is relative to
+  // m_use, so the test is mx > kLazyTau (mx > -inf before any kept key): one
+  // compare against m_thr per tile
   template <int NB>
   __device__ __forceinline__ void rescale(float mx, f32x16 (&s)[NB]) {
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    const float m_new = fmaxf(m_run, m_use + mx);
-    if (__any(m_new > m_run + kLazyTau)) {
+    if (__any(mx > m_thr)) {
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      const float m_new = fmaxf(m_run, m_use + mx);
       const float alpha = (m_run == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       const float m_next = (m_new == -INFINITY) ? 0.f : m_new;
       const float shift = m_next - m_use;
@@ -450,6 +457,7 @@ struct Rows32 {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] -= shift;
       m_run = m_new;
+      m_thr = (m_new == -INFINITY) ? -INFINITY : kLazyTau;
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < D / 32; ++i)
