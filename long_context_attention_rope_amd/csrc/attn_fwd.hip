@@ -429,8 +429,9 @@ struct Rows32 {
       return x;
     }
   }
-  // row max of a tile of s = S·scale·log2(e) - m_use, shared by lanes l and
-  // l^32 (m_use = m_run, or 0 before any kept key)
+  // max of this lane's half of a row's tile of s = S·scale·log2(e) - m_use
+  // (lanes l and l^32 hold the two halves of one row's keys; m_use = m_run,
+  // or 0 before any kept key)
   template <int NB>
   __device__ __forceinline__ float tile_max(const f32x16 (&s)[NB]) const {
     float mx = -INFINITY;
@@ -438,15 +439,18 @@ struct Rows32 {
     for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    return xor32_max(mx);
+    return mx;
   }
   // move the reference max when a row max grew by more than 2^kLazyTau, and
-  // shift this tile's s to the new reference.  The tile max mx is relative to
+  // shift this tile's s to the new reference.  The tile max is relative to
   // m_use, so the test is mx > kLazyTau (mx > -inf before any kept key): one
-  // compare against m_thr per tile
+  // compare against m_thr per tile.  Either half of a row exceeding it sends
+  // the wave into the branch, where the two halves' maxima are combined (the
+  // two lanes of a row must keep one reference)
   template <int NB>
-  __device__ __forceinline__ void rescale(float mx, f32x16 (&s)[NB]) {
-    if (__any(mx > m_thr)) {
+  __device__ __forceinline__ void rescale(float mx_half, f32x16 (&s)[NB]) {
+    if (__any(mx_half > m_thr)) {
+      const float mx = xor32_max(mx_half);
       const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
       const float m_new = fmaxf(m_run, m_use + mx);
       const float alpha = (m_run == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
