@@ -128,7 +128,11 @@ typedef struct {
   const float* cos_tab;   /* tables from lcx_rope_freqs; required if rope_q or rope_k */
   const float* sin_tab;
   int64_t tab_pos0, tab_len;
-  const lcx_rope_cfg* rope; /* optional: supplies the YaRN logit multiplier */
+  const lcx_rope_cfg* rope; /* configuration the rotation came from; supplies the YaRN logit
+                               multiplier.  Required with rope_q or rope_k; optional for
+                               pre-rotated q/k (then pass it, or softmax_scale, whenever the
+                               rotation was YaRN's, or its temperature is not applied);
+                               head_dim must equal d */
   float softmax_scale;      /* 0: (1/sqrt(d))·logit_mult(rope) */
   int32_t causal;           /* must be 1 */
   int64_t window;           /* -1: none; else key kept iff pos_k >= pos_q - window ... */
@@ -153,7 +157,8 @@ typedef struct {
  * (P rounded to bf16); fp32 accumulation and softmax, row sums of P rounded
  * to f16.
  * Errors: INVALID_ARG for NULL q/k/v/o/lse, sizes <= 0 (n_kv may be 0: all
- * rows empty), Hq % Hkv != 0, window < -1, n_sink < 0, tables missing or not
+ * rows empty), Hq % Hkv != 0, window < -1, n_sink < 0, rope_q/rope_k not 0/1,
+ * rope_q or rope_k without rope, rope->head_dim != d, tables missing or not
  * covering the rotated positions, accumulate with a bf16 o, f16 with rope on;
  * UNSUPPORTED for d not 64/128, causal == 0, non-16-byte-aligned rows.
  */
@@ -236,7 +241,8 @@ lcx_status lcx_attn_merge(float* o_acc, float* lse_acc, const float* o_part, con
  * a->lse may be lse_acc).  [CW §5.1-5.4 Ring Attention; kwkr.cn news 38338
  * §2.2 ring computation with online aggregation]
  * Errors: as lcx_attn_fwd, plus INVALID_ARG for chunk <= 0, NULL o_acc/lse_acc,
- * exactly one of o_part/lse_part NULL, a->accumulate != 0.
+ * exactly one of o_part/lse_part NULL, a->accumulate != 0, a->o == o_acc with
+ * o_dtype other than F32.
  */
 lcx_status lcx_attn_fwd_chunked(const lcx_attn_args* a, int64_t chunk, float* o_acc, float* lse_acc,
                                 float* o_part, float* lse_part, hipStream_t stream);
@@ -256,7 +262,7 @@ typedef struct {
   int64_t q_strides[3], k_strides[3], v_strides[3], o_strides[3], do_strides[3]; /* elements */
   int64_t lse_strides[2];  /* elements: batch, head (unit row stride) */
   int64_t q_pos0, k_pos0;  /* absolute positions of row 0 / key 0 */
-  const lcx_rope_cfg* rope; /* optional: supplies the YaRN logit multiplier */
+  const lcx_rope_cfg* rope; /* as in lcx_attn_args: required with unrotate; head_dim == d */
   float softmax_scale;      /* 0: (1/sqrt(d))·logit_mult(rope), as in the forward */
   int32_t causal;           /* must be 1 */
   int64_t window;           /* -1: none (same mask rules as lcx_attn_fwd) */
@@ -291,7 +297,8 @@ typedef struct {
  * n_q = 0, those of the key side (k, v, dk, dv) when n_kv = 0; with no rows
  * dk = dv = 0, with no keys dq = 0.
  * Errors: INVALID_ARG for NULL pointers, bad sizes, Hq % Hkv != 0, window <
- * -1, n_sink < 0, bad dtypes, unrotate without tables covering the positions;
+ * -1, n_sink < 0, bad dtypes, unrotate without rope or without tables covering
+ * the positions, rope->head_dim != d;
  * UNSUPPORTED for d not 64/128, causal == 0, non-16-byte-aligned rows or
  * pointers, a row stride of 2^24 elements or more.
  */

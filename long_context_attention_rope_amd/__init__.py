@@ -161,6 +161,10 @@ def rope_apply_qk(q, k, cos, sin, *, pos0: int = 0, tab_pos0: int = 0, q_out=Non
         q_out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
     if k is not None and k_out is None:
         k_out = torch.empty(k.shape, dtype=out_dtype, device=k.device)
+    for x, y, name in ((q, q_out, "q"), (k, k_out, "k")):
+        if x is not None:
+            _rows4(x, name, dtypes=(torch.bfloat16,))
+            _rows4(y, name + "_out", shape=x.shape, dtypes=(torch.bfloat16, torch.float16))
     ref = q if q is not None else k
     B, _, n, d = ref.shape
     Hq = q.shape[1] if q is not None else 0
@@ -172,10 +176,44 @@ def rope_apply_qk(q, k, cos, sin, *, pos0: int = 0, tab_pos0: int = 0, q_out=Non
     return q_out, k_out
 
 
+def _rows4(t, name, shape=None, dtypes=None):
+    """A [B, H, n, d] tensor whose rows are contiguous (the library takes element
+    strides of the first three dimensions and assumes unit stride in the last)."""
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be 4-D [B, H, n, d], got {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} dtype {t.dtype} not in {dtypes}")
+    if t.shape[3] > 1 and t.stride(3) != 1:
+        raise ValueError(f"{name} rows must be contiguous (stride(-1) == 1)")
+
+
+def _workspace(t, name, shape):
+    """Caller-owned fp32 scratch the C side addresses as a contiguous block."""
+    if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)} (contiguous: {t.is_contiguous()})")
+
+
 def _attn_args(q, k, v, o, lse, *, rope_q, rope_k, cos, sin, tab_pos0, cfg, softmax_scale,
                window, n_sink, q_pos0, k_pos0, accumulate, causal=True):
+    _rows4(q, "q", dtypes=(torch.bfloat16, torch.float16))
     B, Hq, n_q, d = q.shape
+    _rows4(k, "k", dtypes=(torch.bfloat16, torch.float16))
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError(f"k {tuple(k.shape)} does not match q {tuple(q.shape)}")
     Hkv, n_kv = k.shape[1], k.shape[2]
+    if v.dim() == 5:
+        if (v.shape[0], v.shape[1], v.shape[3], v.shape[4]) != (B, Hkv, d, 64) or v.shape[2] * 64 < n_kv \
+                or v.stride(4) != 1 or v.stride(3) != 64 or v.stride(2) != 64 * d:
+            raise ValueError(f"V tiles must be [B, Hkv, >= ceil(n_kv/64), d, 64] with contiguous tiles, "
+                             f"got {tuple(v.shape)}")
+    else:
+        _rows4(v, "v", shape=(B, Hkv, n_kv, d), dtypes=(torch.bfloat16,))
+    _rows4(o, "o", shape=(B, Hq, n_q, d), dtypes=(torch.bfloat16, torch.float32))
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, n_q):
+        raise ValueError(f"lse must be float32 [B, Hq, n_q], got {lse.dtype} {tuple(lse.shape)}")
     a = AttnArgs()
     a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
     a.q_dtype, a.k_dtype = _DT[q.dtype], _DT[k.dtype]
@@ -212,10 +250,9 @@ def _attn_args(q, k, v, o, lse, *, rope_q, rope_k, cos, sin, tab_pos0, cfg, soft
 def pack_v(v, out=None):
     """lcx_attn_pack_v: v [B,Hkv,n,d] bf16 -> tile layout [B,Hkv,ceil(n/64),d,64] float16
     (V converted to f16), accepted by attn_fwd / attn_fwd_chunked / attn_decode in place of v."""
+    _rows4(v, "v", dtypes=(torch.bfloat16,))
     B, Hkv, n, d = v.shape
     T = (n + 63) // 64
-    if v.dtype != torch.bfloat16:
-        raise ValueError("pack_v takes bf16 V")
     if out is None:
         out = torch.empty((B, Hkv, T, d, 64), dtype=torch.float16, device=v.device)
     if tuple(out.shape) != (B, Hkv, T, d, 64) or not out.is_contiguous() or out.dtype != torch.float16:
@@ -268,6 +305,8 @@ def attn_decode(q, k, v, o=None, lse=None, *, n_splits=None, o_part=None, lse_pa
         o_part = torch.empty((n_splits, B, Hq, n_q, d), dtype=torch.float32, device=q.device)
     if lse_part is None:
         lse_part = torch.empty((n_splits, B, Hq, n_q), dtype=torch.float32, device=q.device)
+    _workspace(o_part, "o_part", (n_splits, B, Hq, n_q, d))
+    _workspace(lse_part, "lse_part", (n_splits, B, Hq, n_q))
     a = _attn_args(q, k, v, o, lse, rope_q=rope_q, rope_k=False, cos=cos, sin=sin,
                    tab_pos0=tab_pos0, cfg=rope, softmax_scale=softmax_scale, window=window,
                    n_sink=n_sink, q_pos0=q_pos0, k_pos0=k_pos0, accumulate=False)
@@ -282,6 +321,13 @@ def attn_fwd_chunked(q, k, v, chunk: int, o_acc, lse_acc, o=None, lse=None, *, o
     """lcx_attn_fwd_chunked.  o_acc fp32 [B,Hq,n_q,d] / lse_acc fp32 [B,Hq,n_q] workspace;
     o_part/lse_part (same shapes) select the separate merge pass.  Returns (o, lse)."""
     B, Hq, n_q, d = q.shape
+    _workspace(o_acc, "o_acc", (B, Hq, n_q, d))
+    _workspace(lse_acc, "lse_acc", (B, Hq, n_q))
+    if (o_part is None) != (lse_part is None):
+        raise ValueError("o_part and lse_part go together")
+    if o_part is not None:
+        _workspace(o_part, "o_part", (B, Hq, n_q, d))
+        _workspace(lse_part, "lse_part", (B, Hq, n_q))
     if o is None:
         o = torch.empty((B, Hq, n_q, d), dtype=out_dtype, device=q.device)
     if lse is None:
@@ -296,7 +342,14 @@ def attn_fwd_chunked(q, k, v, chunk: int, o_acc, lse_acc, o=None, lse=None, *, o
 
 def attn_merge(o_acc, lse_acc, o_part, lse_part, o_final=None):
     """lcx_attn_merge over [B,H,rows,d] fp32 tensors (in place into o_acc/lse_acc)."""
+    _rows4(o_acc, "o_acc", dtypes=(torch.float32,))
     B, H, rows, d = o_acc.shape
+    _rows4(o_part, "o_part", shape=(B, H, rows, d), dtypes=(torch.float32,))
+    if o_final is not None:
+        _rows4(o_final, "o_final", shape=(B, H, rows, d), dtypes=(torch.bfloat16, torch.float32))
+    for t, name in ((lse_acc, "lse_acc"), (lse_part, "lse_part")):
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, H, rows):
+            raise ValueError(f"{name} must be float32 [B, H, rows], got {t.dtype} {tuple(t.shape)}")
     if lse_acc.stride(2) != 1 or lse_part.stride(2) != 1:
         raise ValueError("lse rows must be contiguous")
     fdt = _DT[o_final.dtype] if o_final is not None else BF16
@@ -325,10 +378,19 @@ def attn_bwd(q, k, v, o, lse, dout, *, dq=None, dk=None, dv=None, workspace=None
         dv = torch.empty((B, Hkv, n_kv, d), dtype=grad_dtype, device=dev)
     if workspace is None:
         workspace = torch.empty((B, Hq, n_q, 2), dtype=torch.float32, device=dev)
-    if not workspace.is_contiguous() or tuple(workspace.shape) != (B, Hq, n_q, 2):
-        raise ValueError("workspace must be a contiguous fp32 [B, Hq, n_q, 2] tensor")
+    _workspace(workspace, "workspace", (B, Hq, n_q, 2))
     if not (dq.dtype == dk.dtype == dv.dtype):
         raise ValueError("dq, dk, dv must share one dtype")
+    _rows4(q, "q", dtypes=(torch.bfloat16,))
+    _rows4(k, "k", shape=(B, Hkv, n_kv, d), dtypes=(torch.bfloat16,))
+    _rows4(v, "v", shape=(B, Hkv, n_kv, d), dtypes=(torch.bfloat16,))
+    _rows4(o, "o", shape=(B, Hq, n_q, d), dtypes=(torch.bfloat16, torch.float32))
+    _rows4(dout, "dout", shape=(B, Hq, n_q, d), dtypes=(torch.bfloat16,))
+    _rows4(dq, "dq", shape=(B, Hq, n_q, d), dtypes=(torch.bfloat16, torch.float32))
+    _rows4(dk, "dk", shape=(B, Hkv, n_kv, d))
+    _rows4(dv, "dv", shape=(B, Hkv, n_kv, d))
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, n_q):
+        raise ValueError(f"lse must be float32 [B, Hq, n_q], got {lse.dtype} {tuple(lse.shape)}")
     if lse.stride(2) != 1:
         raise ValueError("lse rows must be contiguous")
     a = BwdArgs()

@@ -143,11 +143,18 @@ lcx_status check_attn(const lcx_attn_args* a, bool chunked) {
                                              : "accumulate needs an f32 o");
   if (!(a->softmax_scale >= 0.f) || !std::isfinite(a->softmax_scale))
     return fail(LCX_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0 (0: default)");
+  if (a->rope_q != 0 && a->rope_q != 1) return fail(LCX_ERR_INVALID_ARG, "rope_q must be 0 or 1");
+  if (a->rope_k != 0 && a->rope_k != 1) return fail(LCX_ERR_INVALID_ARG, "rope_k must be 0 or 1");
   if (a->rope) {
     lcx_status st = check_cfg(a->rope);
     if (st != LCX_OK) return st;
+    if (a->rope->head_dim != a->d)
+      return fail(LCX_ERR_INVALID_ARG, "rope head_dim %d differs from d %d", a->rope->head_dim, a->d);
   }
   if (a->rope_q || a->rope_k) {
+    // the tables' configuration also fixes the logit multiplier (YaRN's 1/t):
+    // without it the temperature would be dropped silently
+    if (!a->rope) return fail(LCX_ERR_INVALID_ARG, "rope_q/rope_k need the rope configuration of the tables");
     if (!a->cos_tab || !a->sin_tab) return fail(LCX_ERR_INVALID_ARG, "RoPE tables missing");
     if (a->rope_q && !covers(a->tab_pos0, a->tab_len, a->q_pos0, a->n_q))
       return fail(LCX_ERR_INVALID_ARG, "table rows do not cover the query positions");
@@ -197,9 +204,9 @@ lcx::AttnParams make_params(const lcx_attn_args* a) {
   p.tab_pos0 = a->tab_pos0;
   p.window = a->window;
   double mult = 1.0;
-  if (a->rope) {
-    double th[2 * lcx::kMaxHalfDim], pf;
-    if (a->rope->head_dim <= 4 * lcx::kMaxHalfDim) scheme_freqs(*a->rope, th, &pf, &mult);
+  if (a->rope) {  // head_dim == d (64 or 128), checked
+    double th[lcx::kMaxHalfDim], pf;
+    scheme_freqs(*a->rope, th, &pf, &mult);
   }
   const double sigma = a->softmax_scale > 0.f ? (double)a->softmax_scale : mult / std::sqrt((double)a->d);
   p.scale_log2 = (float)(sigma * 1.4426950408889634074);
@@ -234,8 +241,11 @@ lcx_status check_bwd(const lcx_attn_bwd_args* a) {
   if (a->rope) {
     lcx_status st = check_cfg(a->rope);
     if (st != LCX_OK) return st;
+    if (a->rope->head_dim != a->d)
+      return fail(LCX_ERR_INVALID_ARG, "rope head_dim %d differs from d %d", a->rope->head_dim, a->d);
   }
   if (a->unrotate) {
+    if (!a->rope) return fail(LCX_ERR_INVALID_ARG, "unrotate needs the rope configuration of the tables");
     if (!a->cos_tab || !a->sin_tab) return fail(LCX_ERR_INVALID_ARG, "unrotate needs the RoPE tables");
     if (!covers(a->tab_pos0, a->tab_len, a->q_pos0, a->n_q) || !covers(a->tab_pos0, a->tab_len, a->k_pos0, a->n_kv))
       return fail(LCX_ERR_INVALID_ARG, "table rows do not cover the query and key positions");
@@ -290,9 +300,9 @@ lcx::BwdParams make_bwd_params(const lcx_attn_bwd_args* a) {
   p.tab_pos0 = a->tab_pos0;
   p.window = a->window;
   double mult = 1.0;
-  if (a->rope) {
-    double th[2 * lcx::kMaxHalfDim], pf;
-    if (a->rope->head_dim <= 4 * lcx::kMaxHalfDim) scheme_freqs(*a->rope, th, &pf, &mult);
+  if (a->rope) {  // head_dim == d (64 or 128), checked
+    double th[lcx::kMaxHalfDim], pf;
+    scheme_freqs(*a->rope, th, &pf, &mult);
   }
   const double sigma = a->softmax_scale > 0.f ? (double)a->softmax_scale : mult / std::sqrt((double)a->d);
   p.scale = (float)sigma;
@@ -304,6 +314,29 @@ lcx::BwdParams make_bwd_params(const lcx_attn_bwd_args* a) {
   p.grad_f32 = a->grad_dtype == LCX_F32;
   p.unrotate = a->unrotate;
   return p;
+}
+
+lcx_status check_decode(const lcx_attn_args* a, int32_t n_splits) {
+  lcx_status st = check_attn(a, false);
+  if (st != LCX_OK) return st;
+  if (a->accumulate) return fail(LCX_ERR_INVALID_ARG, "accumulate must be 0 for decode");
+  if (a->n_q > 8) return fail(LCX_ERR_UNSUPPORTED, "decode takes at most 8 new rows (n_q = %lld)", (long long)a->n_q);
+  if ((int64_t)(a->Hq / a->Hkv) * a->n_q > 64)
+    return fail(LCX_ERR_UNSUPPORTED, "decode needs (Hq/Hkv)·n_q <= 64");
+  if (a->rope_k || a->k_dtype != LCX_F16)
+    return fail(LCX_ERR_UNSUPPORTED, "decode reads a pre-rotated f16 K cache (rope_k = 0, k_dtype F16)");
+  if (n_splits < 1 || n_splits > 65535) return fail(LCX_ERR_INVALID_ARG, "n_splits %d outside 1..65535", n_splits);
+  if (a->B > 65535 || a->Hkv > 65535) return fail(LCX_ERR_UNSUPPORTED, "B and Hkv must be <= 65535");
+  return LCX_OK;
+}
+
+lcx_status run_decode(const lcx_attn_args* a, int32_t n_splits, float* o_part, float* lse_part,
+                      hipStream_t stream) {
+  lcx::AttnParams p = make_params(a);
+  lcx::DecodeParams dp{o_part, lse_part, n_splits};
+  hipError_t e = lcx::launch_attn_decode(p, dp, stream);
+  if (e != hipSuccess) return hip_status(e, "decode launch");
+  return hip_status(lcx::launch_decode_combine(p, dp, stream), "combine launch");
 }
 
 }  // namespace
@@ -419,24 +452,12 @@ lcx_status lcx_attn_fwd(const lcx_attn_args* a, hipStream_t stream) {
 
 lcx_status lcx_attn_decode(const lcx_attn_args* a, int32_t n_splits, float* o_part, float* lse_part,
                            hipStream_t stream) {
-  lcx_status st = check_attn(a, false);
+  lcx_status st = check_decode(a, n_splits);
   if (st != LCX_OK) return st;
-  if (a->accumulate) return fail(LCX_ERR_INVALID_ARG, "accumulate must be 0 for decode");
-  if (a->n_q > 8) return fail(LCX_ERR_UNSUPPORTED, "decode takes at most 8 new rows (n_q = %lld)", (long long)a->n_q);
-  if ((int64_t)(a->Hq / a->Hkv) * a->n_q > 64)
-    return fail(LCX_ERR_UNSUPPORTED, "decode needs (Hq/Hkv)·n_q <= 64");
-  if (a->rope_k || a->k_dtype != LCX_F16)
-    return fail(LCX_ERR_UNSUPPORTED, "decode reads a pre-rotated f16 K cache (rope_k = 0, k_dtype F16)");
-  if (n_splits < 1 || n_splits > 65535) return fail(LCX_ERR_INVALID_ARG, "n_splits %d outside 1..65535", n_splits);
-  if (a->B > 65535 || a->Hkv > 65535) return fail(LCX_ERR_UNSUPPORTED, "B and Hkv must be <= 65535");
   if (!o_part || !lse_part) return fail(LCX_ERR_INVALID_ARG, "o_part and lse_part are required");
   if (!aligned16(o_part)) return fail(LCX_ERR_UNSUPPORTED, "o_part must be 16-byte aligned");
   if (a->n_q == 0) return ok();
-  lcx::AttnParams p = make_params(a);
-  lcx::DecodeParams dp{o_part, lse_part, n_splits};
-  hipError_t e = lcx::launch_attn_decode(p, dp, stream);
-  if (e != hipSuccess) return hip_status(e, "decode launch");
-  return hip_status(lcx::launch_decode_combine(p, dp, stream), "combine launch");
+  return run_decode(a, n_splits, o_part, lse_part, stream);
 }
 
 lcx_status lcx_attn_pack_v(const void* v, void* v_tiles, int32_t B, int32_t Hkv, int64_t n,
@@ -504,6 +525,10 @@ lcx_status lcx_attn_fwd_chunked(const lcx_attn_args* a, int64_t chunk, float* o_
     return fail(LCX_ERR_INVALID_ARG, "o_part and lse_part go together");
   if (!aligned16(o_acc) || (o_part && !aligned16(o_part)))
     return fail(LCX_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+  // the final copy is skipped when a->o is the accumulator itself, which
+  // holds fp32
+  if (a->o == (void*)o_acc && a->o_dtype != LCX_F32)
+    return fail(LCX_ERR_INVALID_ARG, "o may alias o_acc only with o_dtype F32");
   if (a->n_q == 0) return ok();
   const int64_t d = a->d, nq = a->n_q;
   const int64_t acc_st[3] = {a->Hq * nq * d, nq * d, d};

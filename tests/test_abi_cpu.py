@@ -264,3 +264,79 @@ def test_merge_rejects(lcx):
     f = lcx._lib.lcx_attn_merge
     assert f(None, FAKE, FAKE, FAKE, 1, 1, 64, 64, s3, s3, s2, s2, None, 0, None, None) == 1
     assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 62, s3, s3, s2, s2, None, 0, None, None) == 2
+
+
+# the rope configuration must describe the rotation the kernel applies: its
+# head_dim is the call's d, and a fused rotation cannot run without it (YaRN's
+# temperature comes from it, "上下文窗口扩展技术" §2.4)
+def test_attn_fwd_rope_cfg_checks(lcx):
+    cfg64 = lcx.rope_cfg("yarn", 500000.0, 64, 128, 512)
+    cfg128 = lcx.rope_cfg("yarn", 500000.0, 128, 128, 512)
+    tabs = dict(cos_tab=FAKE, sin_tab=FAKE, tab_len=256)
+    f = lcx._lib.lcx_attn_fwd
+    assert f(ctypes.byref(_args(lcx, rope_q=1, **tabs)), None) == 1        # no rope with rope_q
+    assert f(ctypes.byref(_args(lcx, rope_k=1, **tabs)), None) == 1        # no rope with rope_k
+    assert b"rope configuration" in lcx._lib.lcx_last_error()
+    assert f(ctypes.byref(_args(lcx, rope=ctypes.pointer(cfg128))), None) == 1  # head_dim 128, d 64
+    assert b"head_dim" in lcx._lib.lcx_last_error()
+    assert f(ctypes.byref(_args(lcx, rope_q=1, rope=ctypes.pointer(cfg128), **tabs)), None) == 1
+    assert f(ctypes.byref(_args(lcx, rope_q=2, rope=ctypes.pointer(cfg64), **tabs)), None) == 1
+    # decode shares the checks
+    a = _args(lcx, n_q=4, k_dtype=lcx.F16, rope_q=1, **tabs)
+    assert lcx._lib.lcx_attn_decode(ctypes.byref(a), 8, FAKE, FAKE, None) == 1
+    a = _args(lcx, n_q=4, k_dtype=lcx.F16, rope=ctypes.pointer(cfg128))
+    assert lcx._lib.lcx_attn_decode(ctypes.byref(a), 8, FAKE, FAKE, None) == 1
+
+
+def test_attn_bwd_rope_cfg_checks(lcx):
+    cfg128 = lcx.rope_cfg("yarn", 500000.0, 128, 128, 512)
+    f = lcx._lib.lcx_attn_bwd
+    a = _bwd_args(lcx, unrotate=1, cos_tab=FAKE, sin_tab=FAKE, tab_len=256)
+    assert f(ctypes.byref(a), None) == 1 and b"rope configuration" in lcx._lib.lcx_last_error()
+    a = _bwd_args(lcx, rope=ctypes.pointer(cfg128))
+    assert f(ctypes.byref(a), None) == 1 and b"head_dim" in lcx._lib.lcx_last_error()
+
+
+def test_chunked_rejects_bf16_output_in_the_accumulator(lcx):
+    # finalize skips the copy when o is o_acc: only an fp32 o may alias it
+    a = _args(lcx, o=FAKE + 4096)
+    assert lcx._lib.lcx_attn_fwd_chunked(ctypes.byref(a), 64, FAKE + 4096, FAKE, None, None, None) == 1
+    assert b"o_acc" in lcx._lib.lcx_last_error()
+
+
+def test_binding_rejects_bad_tensors_before_the_call(lcx):
+    # CPU tensors: every case is rejected in Python before anything reaches C
+    import torch
+    bf, f32 = torch.bfloat16, torch.float32
+    q = torch.zeros(1, 4, 256, 64, dtype=bf)
+    k = torch.zeros(1, 1, 256, 64, dtype=bf)
+    v = torch.zeros(1, 1, 256, 64, dtype=bf)
+    o_acc = torch.zeros(1, 4, 256, 64, dtype=f32)
+    l_acc = torch.zeros(1, 4, 256, dtype=f32)
+    bad = [
+        lambda: lcx.attn_fwd(q.transpose(2, 3), k, v),                       # rows not contiguous
+        lambda: lcx.attn_fwd(q, k[..., :32], v),                             # k's d differs
+        lambda: lcx.attn_fwd(q, k, v.float()),                               # v dtype
+        lambda: lcx.attn_fwd(q, k, v, o=torch.zeros(1, 4, 255, 64, dtype=bf)),
+        lambda: lcx.attn_fwd(q, k, v, lse=torch.zeros(1, 4, 256, dtype=bf)),
+        lambda: lcx.attn_fwd(q, k, torch.zeros(1, 1, 3, 64, 64, dtype=torch.float16)),  # too few tiles
+        lambda: lcx.attn_fwd_chunked(q, k, v, 64, o_acc[:, :, :128], l_acc),
+        lambda: lcx.attn_fwd_chunked(q, k, v, 64, o_acc.to(bf), l_acc),
+        lambda: lcx.attn_fwd_chunked(q, k, v, 64, o_acc.transpose(2, 3).contiguous().transpose(2, 3), l_acc),
+        lambda: lcx.attn_fwd_chunked(q, k, v, 64, o_acc, l_acc, o_part=o_acc.clone()),
+        lambda: lcx.attn_fwd_chunked(q, k, v, 64, o_acc, l_acc, o_part=o_acc[:, :2], lse_part=l_acc),
+        lambda: lcx.attn_decode(q[:, :, :4], k.half(), v, n_splits=4,
+                                o_part=torch.zeros(4, 1, 4, 4, 32, dtype=f32)),
+        lambda: lcx.attn_decode(q[:, :, :4], k.half(), v, n_splits=4,
+                                lse_part=torch.zeros(3, 1, 4, 4, dtype=f32)),
+        lambda: lcx.attn_merge(o_acc, l_acc, o_acc[:, :, :100], l_acc),
+        lambda: lcx.attn_merge(o_acc, l_acc, o_acc, l_acc.to(bf)),
+        lambda: lcx.pack_v(v.transpose(2, 3)),
+        lambda: lcx.rope_apply_qk(None, k, None, None, k_out=torch.zeros(1, 1, 255, 64, dtype=torch.float16)),
+        lambda: lcx.attn_bwd(q, k, v, q, l_acc, q, workspace=torch.zeros(1, 4, 256, 3, dtype=f32)),
+        lambda: lcx.attn_bwd(q, k, v, q, l_acc, q.transpose(2, 3).contiguous().transpose(2, 3)),
+    ]
+    for i, fn in enumerate(bad):
+        with pytest.raises(ValueError):
+            fn()
+

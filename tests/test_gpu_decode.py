@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 import torch
 
+import fixtures
 from fixtures import workloads as W
 from tests import gpu_util as U
 
@@ -92,3 +93,34 @@ def test_decode_two_batches(lcx):
         torch.cuda.synchronize()
         U.check(o.cpu().numpy().reshape(-1, w.d), lse.cpu().numpy().reshape(-1), o_ref, l_ref,
                 f"decode/B=2/splits={ns}")
+
+
+@pytest.mark.parametrize("n_q", [1, 8])
+def test_decode_at_the_benchmarked_shape(lcx, n_q):
+    # the configuration the decode benchmark times: the 70B-shaped GQA cache at
+    # its full length ("上下文擴充套件" KV Cache 的視訊記憶體架構; 128K, "上下文窗口扩展技术"
+    # §3), 131072 pre-rotated f16 keys per KV head, V tiles, the default 32
+    # splits per KV head (64 tiles each), the new rows' tables built for their
+    # positions only; every (head, new row) against the oracle
+    w = W.LLAMA70B_128K
+    U.log(f"decode at the benchmarked shape, n_q={n_q}")
+    q = fixtures.normal_bf16(w.seed, fixtures.Q_ID, (w.B, w.Hq, n_q, w.d))
+    _, k, v = U.inputs(w, n_q=1)
+    cfg = lcx.rope_cfg(w.scheme, w.base, w.d, w.L_train, w.L_target, w.cur_len, w.alpha, w.beta)
+    cos_all, sin_all = lcx.rope_tables(cfg, w.n, device=U.dev())
+    _, kr = lcx.rope_apply_qk(None, U.to_dev(k), cos_all, sin_all)
+    vt = lcx.pack_v(U.to_dev(v))
+    del cos_all, sin_all
+    qp0 = w.n - n_q
+    cos, sin = lcx.rope_tables(cfg, n_q, pos0=qp0, device=U.dev())
+    ns = lcx.decode_splits(w.B, w.Hkv, w.n, w.d)
+    assert ns == 32
+    o, lse = lcx.attn_decode(U.to_dev(q), kr, vt, n_splits=ns, rope_q=True, cos=cos, sin=sin,
+                             tab_pos0=qp0, rope=cfg, q_pos0=qp0)
+    torch.cuda.synchronize()
+    bb = np.zeros(w.Hq * n_q, np.int32)
+    hh = np.repeat(np.arange(w.Hq), n_q).astype(np.int32)
+    rr = np.tile(np.arange(n_q), w.Hq)
+    o_ref, l_ref = U.oracle_rows(w, q, k, v, bb, hh, rr, q_pos0=qp0)
+    U.check(o.float().cpu().numpy().reshape(-1, w.d), lse.cpu().numpy().reshape(-1), o_ref, l_ref,
+            f"decode/70b_128k/n_q={n_q}/splits={ns}")

@@ -138,6 +138,21 @@ def test_yarn_is_by_parts_plus_temperature():
     np.testing.assert_allclose(1 / lm2 - 1, 2 * (1 / lm - 1), rtol=1e-13)
 
 
+def test_yarn_temperature_golden():
+    # the oracle's logit multiplier is 1/t at the page's t for every listed s
+    # (pins the coefficient 0.1 and the natural log, which the log-linearity
+    # check above leaves open), and the 8B workload's softmax scale
+    g = _golden("yarn_temperature.txt")
+    rows = [r for r in g["rows"] if len(r) == 3]
+    assert len(rows) == 5
+    for lt, lg, t in rows:
+        th, pf, lm = oracle.rope_freqs("yarn", 500000.0, 128, int(lt), int(lg))
+        assert 1.0 / lm == pytest.approx(float(t), rel=5e-16, abs=0), (lt, lg)
+        assert pf == 1.0
+    _, _, lm4 = oracle.rope_freqs("yarn", 500000.0, 128, 8192, 32768)
+    assert abs(lm4 / np.sqrt(128.0) - g["sigma_d128_s4"]) < 5e-8
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_dynamic_ntk(d):
     base, L = 500000.0, 8192
