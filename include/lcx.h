@@ -3,9 +3,11 @@
  *
  * C ABI of liblcx.so.  Plain pointers and sizes only.  Device pointers are
  * HIP device memory owned by the caller; host pointers are ordinary memory.
- * The library allocates no device memory, keeps no global state, never
- * synchronises and never creates streams: all device work is enqueued on the
- * caller's `stream`.  Every argument check happens before anything is
+ * The library allocates no device memory, never synchronises and never
+ * creates streams: all device work is enqueued on the caller's `stream`.  Its
+ * only state is the fixed device scratch of lcx_attn_decode_noalloc (one
+ * copy per device, held until the process ends) and that array's address per
+ * device.  Every argument check happens before anything is
  * enqueued; a non-OK return enqueues nothing (LCX_ERR_HIP: a launch was
  * rejected by the runtime).  Faults inside kernels surface at the caller's
  * next synchronisation.  No C++ exception crosses this boundary.
@@ -187,6 +189,35 @@ lcx_status lcx_attn_fwd(const lcx_attn_args* a, hipStream_t stream);
  */
 lcx_status lcx_attn_decode(const lcx_attn_args* a, int32_t n_splits, float* o_part, float* lse_part,
                            hipStream_t stream);
+
+/* Size of the static device scratch that lcx_attn_decode_noalloc keeps the
+ * split partials in: 16 MiB per device. */
+#define LCX_DECODE_SCRATCH_BYTES (16u << 20)
+
+/*
+ * lcx_attn_decode without a caller workspace, for callers that cannot
+ * allocate device memory (code being captured into a HIP graph, tight serving
+ * loops, harnesses that forbid hipMalloc): the split partials live in a
+ * file-scope device array of LCX_DECODE_SCRATCH_BYTES per device instead of
+ * o_part/lse_part.  Same arguments, kernels and results as lcx_attn_decode
+ * with the same n_splits (bit for bit); makes no hipMalloc, hipFree or other
+ * allocating call.  The scratch address of the current device is looked up
+ * on the first call on that device (hipGetSymbolAddress) and kept.
+ *   a, n_splits  as for lcx_attn_decode; the device is the current one, and
+ *                `stream` must belong to it.
+ * The partials need n_splits·B·Hq·n_q·(d + 1)·4 bytes (the O part rounded up
+ * to 256); more than LCX_DECODE_SCRATCH_BYTES is rejected.  The default split
+ * count of the Python binding (about 256 workgroups over B·Hkv for d = 128,
+ * 512 for d = 64) needs at most 8.5 MiB for any shape decode accepts.
+ * Every call on one device shares that device's array and leaves its
+ * partials there: calls that may overlap on one device (different streams,
+ * different host threads) race and must be ordered by the caller.  Nothing
+ * in the array needs clearing (each call writes every partial it reads).
+ * Errors: as lcx_attn_decode (without the workspace checks), plus
+ * UNSUPPORTED when the partials exceed the scratch; LCX_ERR_HIP when the
+ * current device cannot be queried or the scratch address not looked up.
+ */
+lcx_status lcx_attn_decode_noalloc(const lcx_attn_args* a, int32_t n_splits, hipStream_t stream);
 
 /*
  * Layout step for the PV product (V is not rotated): V converted to f16 and

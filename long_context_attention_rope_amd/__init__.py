@@ -83,6 +83,9 @@ _lib.lcx_attn_fwd_chunked.restype = ctypes.c_int
 _lib.lcx_attn_pack_v.argtypes = [_vp, _vp, _i32, _i32, _i64, _i32, _P3, _vp]
 _lib.lcx_attn_decode.argtypes = [ctypes.POINTER(AttnArgs), _i32, _vp, _vp, _vp]
 _lib.lcx_attn_decode.restype = ctypes.c_int
+_lib.lcx_attn_decode_noalloc.argtypes = [ctypes.POINTER(AttnArgs), _i32, _vp]
+_lib.lcx_attn_decode_noalloc.restype = ctypes.c_int
+DECODE_SCRATCH_BYTES = 16 << 20  # LCX_DECODE_SCRATCH_BYTES
 _lib.lcx_attn_pack_v.restype = ctypes.c_int
 _lib.lcx_attn_bwd.argtypes = [ctypes.POINTER(BwdArgs), _vp]
 _lib.lcx_attn_bwd.restype = ctypes.c_int
@@ -311,6 +314,22 @@ def attn_decode(q, k, v, o=None, lse=None, *, n_splits=None, o_part=None, lse_pa
                    tab_pos0=tab_pos0, cfg=rope, softmax_scale=softmax_scale, window=window,
                    n_sink=n_sink, q_pos0=q_pos0, k_pos0=k_pos0, accumulate=False)
     _check(_lib.lcx_attn_decode(ctypes.byref(a), n_splits, _ptr(o_part), _ptr(lse_part), _stream(q)))
+    return o, lse
+
+
+def attn_decode_noalloc(q, k, v, o, lse, *, n_splits=None, rope_q=False, cos=None, sin=None, tab_pos0=0,
+                        rope=None, softmax_scale=0.0, window=-1, n_sink=0, q_pos0=0, k_pos0=0):
+    """lcx_attn_decode_noalloc: attn_decode with the split partials in the library's
+    static device scratch (no workspace).  o [B,Hq,n_q,d] and lse [B,Hq,n_q] are the
+    caller's outputs; nothing is allocated.  Calls that overlap on one device race."""
+    B, Hq, n_q, d = q.shape
+    Hkv, n_kv = k.shape[1], k.shape[2]
+    if n_splits is None:
+        n_splits = decode_splits(B, Hkv, n_kv, d)
+    a = _attn_args(q, k, v, o, lse, rope_q=rope_q, rope_k=False, cos=cos, sin=sin,
+                   tab_pos0=tab_pos0, cfg=rope, softmax_scale=softmax_scale, window=window,
+                   n_sink=n_sink, q_pos0=q_pos0, k_pos0=k_pos0, accumulate=False)
+    _check(_lib.lcx_attn_decode_noalloc(ctypes.byref(a), n_splits, _stream(q)))
     return o, lse
 
 

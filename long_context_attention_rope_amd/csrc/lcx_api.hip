@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "lcx.h"
 #include "lcx_internal.h"
@@ -339,6 +340,35 @@ lcx_status run_decode(const lcx_attn_args* a, int32_t n_splits, float* o_part, f
   return hip_status(lcx::launch_decode_combine(p, dp, stream), "combine launch");
 }
 
+// Device scratch of lcx_attn_decode_noalloc (the split partials), a
+// file-scope array so that the entry point allocates nothing.  Each device
+// the library runs on holds its own copy until the process ends.  In host
+// code `scratch` only names the symbol: its device address is looked up once
+// per device with that device current and kept in g_scratch_dev, which is
+// what kernels receive.
+static __device__ __align__(256) char scratch[LCX_DECODE_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+char* g_scratch_dev[kMaxDevices];
+
+lcx_status decode_scratch(char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(LCX_ERR_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(LCX_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_dev[dev] = static_cast<char*>(ptr);
+  }
+  *out = g_scratch_dev[dev];
+  return LCX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -458,6 +488,27 @@ lcx_status lcx_attn_decode(const lcx_attn_args* a, int32_t n_splits, float* o_pa
   if (!aligned16(o_part)) return fail(LCX_ERR_UNSUPPORTED, "o_part must be 16-byte aligned");
   if (a->n_q == 0) return ok();
   return run_decode(a, n_splits, o_part, lse_part, stream);
+}
+
+lcx_status lcx_attn_decode_noalloc(const lcx_attn_args* a, int32_t n_splits, hipStream_t stream) {
+  lcx_status st = check_decode(a, n_splits);
+  if (st != LCX_OK) return st;
+  if (a->n_q == 0) return ok();
+  // partials: O fp32 [n_splits][B][Hq][n_q][d], then (256-byte aligned) LSE
+  // fp32 [n_splits][B][Hq][n_q]; every slot is written by the decode kernel
+  // before the combine pass reads it, so nothing needs clearing
+  const uint64_t rows = (uint64_t)n_splits * (uint64_t)a->B * (uint64_t)a->Hq * (uint64_t)a->n_q;
+  const uint64_t o_bytes = (rows * (uint64_t)a->d * 4u + 255u) & ~(uint64_t)255u;
+  const uint64_t need = o_bytes + rows * 4u;
+  if (need > LCX_DECODE_SCRATCH_BYTES)
+    return fail(LCX_ERR_UNSUPPORTED,
+                "decode partials need %llu bytes; the static scratch holds %llu (fewer splits, rows or heads)",
+                (unsigned long long)need, (unsigned long long)LCX_DECODE_SCRATCH_BYTES);
+  char* base = nullptr;
+  st = decode_scratch(&base);
+  if (st != LCX_OK) return st;
+  return run_decode(a, n_splits, reinterpret_cast<float*>(base),
+                    reinterpret_cast<float*>(base + o_bytes), stream);
 }
 
 lcx_status lcx_attn_pack_v(const void* v, void* v_tiles, int32_t B, int32_t Hkv, int64_t n,

@@ -29,7 +29,8 @@ def _declared():
 
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["lcx_rope_freqs", "lcx_rope_apply_qk", "lcx_attn_fwd",
-                                  "lcx_attn_decode", "lcx_attn_pack_v", "lcx_attn_merge", "lcx_attn_bwd",
+                                  "lcx_attn_decode", "lcx_attn_decode_noalloc", "lcx_attn_pack_v",
+                                  "lcx_attn_merge", "lcx_attn_bwd",
                                   "lcx_attn_fwd_chunked", "lcx_status_string", "lcx_last_error"])
 
 
@@ -340,3 +341,21 @@ def test_binding_rejects_bad_tensors_before_the_call(lcx):
         with pytest.raises(ValueError):
             fn()
 
+
+def test_decode_noalloc_rejects_before_any_device_call(lcx):
+    # the argument checks of lcx_attn_decode apply, and partials beyond the
+    # static scratch are refused before the device is queried (these calls
+    # reach no HIP function, so they run without a GPU)
+    f = lcx._lib.lcx_attn_decode_noalloc
+    assert f(None, 8, None) == 1
+    assert f(ctypes.byref(_args(lcx, n_q=4, k_dtype=lcx.F16)), 0, None) == 1       # n_splits
+    assert f(ctypes.byref(_args(lcx, n_q=4)), 8, None) == 2                        # bf16 K
+    assert f(ctypes.byref(_args(lcx, n_q=9, k_dtype=lcx.F16)), 8, None) == 2       # rows
+    # 4 heads x 4 rows x (64 + 1) x 4 B per split: 4 KiB + 64 B; 16 MiB / that < 4033
+    big = _args(lcx, n_q=4, k_dtype=lcx.F16)
+    assert f(ctypes.byref(big), 4033, None) == 2
+    msg = lcx._lib.lcx_last_error().decode()
+    assert "scratch" in msg and str(16 << 20) in msg
+    assert lcx.DECODE_SCRATCH_BYTES == 16 << 20
+    src = open(HEADER).read()
+    assert "#define LCX_DECODE_SCRATCH_BYTES (16u << 20)" in src
