@@ -349,6 +349,47 @@ def bench_decode(args, w):
     print(json.dumps(out), flush=True)
 
 
+def bench_table(args, w):
+    """The cos/sin table pass alone (lcx_rope_freqs for the layer's n positions):
+    HBM write-bound, 8 bytes per (position, pair)."""
+    import numpy as np
+    import torch
+
+    import long_context_attention_rope_amd as lcx
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = lcx.rope_cfg(w.scheme, w.base, w.d, w.L_train, w.L_target, w.cur_len, w.alpha, w.beta)
+    half = w.d // 2
+    cos = torch.empty((w.n, half), dtype=torch.float32, device=dev)
+    sin = torch.empty_like(cos)
+    stream = torch.cuda.current_stream(dev)
+    steps = max(args.steps, 20)
+    for _ in range(max(args.warmup, 3)):
+        lcx.rope_freqs(cfg, cos, sin, 0)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        lcx.rope_freqs(cfg, cos, sin, 0)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+    nbytes = w.n * half * 8
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "RoPE cos/sin table HBM GB/s (fp32 cos and sin per position and pair, written once)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": max(args.warmup, 3),
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f64", "data": "synthetic",
+        "config": {"workload": w.name + "_rope_table", "positions": w.n, "pairs": half, "rope": w.scheme},
+        "roofline": {"kernel": "rope_table_kernel", "bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline_bwd(w, m: int):
     """The oracle's backward pass (dq, dk, dv, every element) on the first m
     positions of every head of the layer: a causal prefix of the same shape."""
@@ -473,6 +514,8 @@ def main():
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass (lcx_attn_bwd) of this layer instead; --cpu-rows is then "
                          "the length of the prefix the oracle differentiates (default 5120)")
+    ap.add_argument("--table", action="store_true",
+                    help="time the cos/sin table pass (lcx_rope_freqs) for this layer's positions instead")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-merge-check", dest="merge_check", action="store_false",
                     help="skip timing the merge pass on this layer's partial sizes")
@@ -501,6 +544,8 @@ def main():
         args.warmup = 1 if w.chunk else 3
     if args.cpu_rows is None:
         args.cpu_rows = 640 if w.chunk else (5120 if args.bwd else 16384)
+    if args.table:
+        return bench_table(args, w)
     if args.bwd:
         return bench_backward(args, w)
     if w.chunk:

@@ -6,6 +6,8 @@
 // φ_{m,i} = m·θ_i; PI scales m by L_train/L_target, "上下文窗口扩展技术：从 4K 到
 // 1M" §2.1).  The angle is formed and evaluated in fp64 and rounded once to
 // fp32: at positions near 2^20 an fp32 angle would already be off by ~0.06 rad.
+// Within a run of positions the angles advance by the fp64 angle-addition
+// recurrence (below).
 //
 // Rotation: adjacent pairs (x_{2i}, x_{2i+1}) -> (x_{2i}c - x_{2i+1}s,
 // x_{2i}s + x_{2i+1}c) (same page, 技術原理: R(m) turns each pair (2i, 2i+1)).
@@ -16,23 +18,46 @@
 
 namespace lcx {
 
+// Positions are taken in runs of kRun consecutive rows per pair: the first
+// angle of a run, ((pos0 + r0)·factor)·theta'_i, is formed and evaluated in
+// fp64 (sincos), the following ones by the fp64 angle-addition recurrence
+//   cos(a + delta) = cos a·cos delta - sin a·sin delta,
+//   sin(a + delta) = sin a·cos delta + cos a·sin delta,
+// with delta = factor·theta'_i, also from fp64 sincos.  Each step adds about
+// one fp64 rounding (2^-53 relative), so after kRun steps the values differ
+// from the directly evaluated ones by ~1e-14, against the 2^-24 of the fp32
+// rounding that follows; two sincos per kRun entries instead of one per entry
+// leave the kernel bound by its HBM writes.  Lanes take consecutive pairs of
+// one run, so each row segment is written by consecutive lanes.
+constexpr int kRun = 32;
+
 __global__ __launch_bounds__(256) void rope_table_kernel(RopeTableParams p) {
-  const int64_t total = p.n_pos * (int64_t)p.half;
+  const int64_t n_runs = (p.n_pos + kRun - 1) / kRun;
+  const int64_t total = n_runs * (int64_t)p.half;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
-    const int64_t r = e / p.half;
-    const int i = (int)(e - r * p.half);
-    const double pos = (double)(p.pos0 + r) * p.pos_factor;
-    const double phi = pos * p.theta[i];
-    double sv, cv;
-    sincos(phi, &sv, &cv);
-    p.cos_tab[e] = (float)cv;
-    p.sin_tab[e] = (float)sv;
+    const int64_t run = e / p.half;
+    const int i = (int)(e - run * p.half);
+    const int64_t r0 = run * kRun;
+    const double phi0 = ((double)(p.pos0 + r0) * p.pos_factor) * p.theta[i];
+    double s, c, sd, cd;
+    sincos(phi0, &s, &c);
+    sincos(p.pos_factor * p.theta[i], &sd, &cd);
+    const int rows = (int)(p.n_pos - r0 < kRun ? p.n_pos - r0 : kRun);
+    float* cp = p.cos_tab + r0 * p.half + i;
+    float* sp = p.sin_tab + r0 * p.half + i;
+    for (int r = 0; r < rows; ++r) {
+      cp[(int64_t)r * p.half] = (float)c;
+      sp[(int64_t)r * p.half] = (float)s;
+      const double cn = c * cd - s * sd;
+      s = s * cd + c * sd;
+      c = cn;
+    }
   }
 }
 
 hipError_t launch_rope_table(const RopeTableParams& p, hipStream_t s) {
-  const int64_t total = p.n_pos * (int64_t)p.half;
+  const int64_t total = (p.n_pos + kRun - 1) / kRun * (int64_t)p.half;
   if (total == 0) return hipSuccess;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
