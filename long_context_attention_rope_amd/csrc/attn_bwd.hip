@@ -229,7 +229,7 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(const BwdParams p) {
     const int64_t i = grow % p.n_q;
     const int64_t bh = grow / p.n_q;
     const int64_t h = bh % p.Hq, b = bh / p.Hq;
-    const u32x4 g = *reinterpret_cast<const u32x4*>(p.dout + b * p.dos_b + h * p.dos_h + i * p.dos_s + c0);
+    const u32x4 g = load_once(reinterpret_cast<const u32x4*>(p.dout + b * p.dos_b + h * p.dos_h + i * p.dos_s + c0));
     float gv[8], ov[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -238,16 +238,16 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(const BwdParams p) {
     }
     if (p.o_f32) {
       const float* op = static_cast<const float*>(p.o) + b * p.os_b + h * p.os_h + i * p.os_s + c0;
-      const f32x4 a = *reinterpret_cast<const f32x4*>(op);
-      const f32x4 c = *reinterpret_cast<const f32x4*>(op + 4);
+      const f32x4 a = load_once(reinterpret_cast<const f32x4*>(op));
+      const f32x4 c = load_once(reinterpret_cast<const f32x4*>(op + 4));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         ov[e] = a[e];
         ov[4 + e] = c[e];
       }
     } else {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.o) + b * p.os_b +
-                                                      h * p.os_h + i * p.os_s + c0);
+      const u32x4 w = load_once(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.o) + b * p.os_b +
+                                                               h * p.os_h + i * p.os_s + c0));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         ov[2 * e] = bf16lo(w[e]);

@@ -44,6 +44,7 @@
 //    are dispatched consecutively to the same XCD so they share K/V in L2.
 #include "attn_tile.h"
 
+
 namespace lcx {
 
 namespace {
@@ -118,7 +119,7 @@ __device__ __forceinline__ void load_q(const AttnParams& p, const uint16_t* qbas
 // of load i fills row r = (wave·LPW + i)·RPL + L / CPR, slot L % CPR, with
 // the row's chunk (L % CPR) ^ swz(r).  The resource starts at the tile's first
 // key and ends at the last key, so rows past the end land as zeros.
-template <int D, int NW, bool K_SWZ>
+template <int D, int NW, bool K_SWZ, bool STREAM = false>
 struct LdsCopy {
   using T = Tile<D, NW>;
   const uint16_t* base;
@@ -147,7 +148,10 @@ struct LdsCopy {
 #pragma unroll
     for (int i = 0; i < T::LPW; ++i) {
       const uint32_t la = (uint32_t)(uintptr_t)(lds_void*)lds + (uint32_t)((row0 + i * T::RPL) * D * 2);
-      lds_copy16(r, off[i], __builtin_amdgcn_readfirstlane(la));
+      if constexpr (STREAM)
+        lds_copy16_stream(r, off[i], __builtin_amdgcn_readfirstlane(la));
+      else
+        lds_copy16(r, off[i], __builtin_amdgcn_readfirstlane(la));
     }
   }
 };
@@ -159,7 +163,7 @@ struct LdsCopy {
 // key), so the resource covers exactly one tile.
 __device__ __forceinline__ int vt_swz(int r) { return (r >> 1) & 7; }
 
-template <int D, int NW>
+template <int D, int NW, bool STREAM = false>
 struct LdsCopyVT {
   static constexpr int LPW = D * 128 / 1024 / NW;
   static_assert(LPW >= 1 && D * 128 == LPW * NW * 1024, "V tile split");
@@ -181,7 +185,10 @@ struct LdsCopyVT {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const uint32_t la = (uint32_t)(uintptr_t)(lds_void*)lds + (uint32_t)((row0 + i * 8) * BN * 2);
-      lds_copy16(r, off[i], __builtin_amdgcn_readfirstlane(la));
+      if constexpr (STREAM)
+        lds_copy16_stream(r, off[i], __builtin_amdgcn_readfirstlane(la));
+      else
+        lds_copy16(r, off[i], __builtin_amdgcn_readfirstlane(la));
     }
   }
 };
@@ -750,9 +757,10 @@ __global__ __launch_bounds__(64 * NW) void attn_decode_kernel(const AttnParams p
   const int ntl = (int)((int64_t)(split + 1) * bt.ntl / dp.n_splits) - t_begin;
   auto j0_of = [&](int t) { return bt.j0(t_begin + t); };
 
-  LdsCopy<D, NW, true> kcp;
-  LdsCopy<D, NW, false> vcp;
-  LdsCopyVT<D, NW> vtcp;
+  // the cache is read once per step: streaming copies
+  LdsCopy<D, NW, true, true> kcp;
+  LdsCopy<D, NW, false, true> vcp;
+  LdsCopyVT<D, NW, true> vtcp;
   kcp.init(p.k + b * p.ks_b + hkv * p.ks_h, p.ks_s, p.n_kv, wave, lane);
   if constexpr (VT)
     vtcp.init(p.v + b * p.vs_b + hkv * p.vs_h, wave, lane);

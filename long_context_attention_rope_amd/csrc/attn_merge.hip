@@ -51,8 +51,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams p, int rows
   }
   float* oa = p.o_acc + b * p.as_b + h * p.as_h + r * p.as_s + 4 * c;
   const float* ob = p.o_part + b * p.ps_b + h * p.ps_h + r * p.ps_s + 4 * c;
-  const f32x4 va = *reinterpret_cast<const f32x4*>(oa);
-  const f32x4 vb = *reinterpret_cast<const f32x4*>(ob);
+  const f32x4 va = load_once(reinterpret_cast<const f32x4*>(oa));
+  const f32x4 vb = load_once(reinterpret_cast<const f32x4*>(ob));
   f32x4 o;
 #pragma unroll
   for (int e = 0; e < 4; ++e) o[e] = (wa == 0.f ? 0.f : wa * va[e]) + (wb == 0.f ? 0.f : wb * vb[e]);
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinalizeParams p) {
   const int64_t bh = flat / p.rows;
   const int h = (int)(bh % p.H), b = (int)(bh / p.H);
   if (p.copy_o) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(p.o_acc + b * p.as_b + h * p.as_h + r * p.as_s + 4 * c);
+    const f32x4 v = load_once(reinterpret_cast<const f32x4*>(p.o_acc + b * p.as_b + h * p.as_h + r * p.as_s + 4 * c));
     if (p.o_f32) {
       *reinterpret_cast<f32x4*>(static_cast<float*>(p.o) + b * p.os_b + h * p.os_h + r * p.os_s + 4 * c) = v;
     } else {
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const AttnParams p,
     const float ls = dp.lse_part[sp * rows_all + row];
     if (ls == -INFINITY) continue;  // an empty partial (also every partial when mx is -inf)
     const float w = expf(ls - mx);
-    const f32x4 o = *reinterpret_cast<const f32x4*>(dp.o_part + (sp * rows_all + row) * D + 4 * c);
+    const f32x4 o = load_once(reinterpret_cast<const f32x4*>(dp.o_part + (sp * rows_all + row) * D + 4 * c));
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] += w * o[e];
     l += w;

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void pack_v_kernel(const PackVParams p) {
   for (int idx = threadIdx.x; idx < kTileKeys * (D / 8); idx += 256) {
     const int key = idx / (D / 8), ch = idx % (D / 8);
     u32x4 w = {0u, 0u, 0u, 0u};
-    if (j0 + key < p.n) w = *reinterpret_cast<const u32x4*>(src + (j0 + key) * p.vs_s + ch * 8);
+    if (j0 + key < p.n) w = load_once(reinterpret_cast<const u32x4*>(src + (j0 + key) * p.vs_s + ch * 8));
     *reinterpret_cast<u32x4*>(tile + key * STR + ch * 8) = w;
   }
   __syncthreads();

@@ -79,14 +79,14 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(RopeApplyLaunch L) {
   const int c = (int)(t - srow * cpr);
   const int half = p0.d >> 1;
   const int64_t trow = p0.pos0 + srow - p0.tab_pos0;
-  const f32x4 cs = *reinterpret_cast<const f32x4*>(p0.cos_tab + trow * half + c * 4);
-  const f32x4 sn = *reinterpret_cast<const f32x4*>(p0.sin_tab + trow * half + c * 4);
+  const f32x4 cs = load_once(reinterpret_cast<const f32x4*>(p0.cos_tab + trow * half + c * 4));
+  const f32x4 sn = load_once(reinterpret_cast<const f32x4*>(p0.sin_tab + trow * half + c * 4));
   for (int sl = 0; sl < L.n_slots; ++sl) {
     const RopeApplyParams& p = L.slot[sl];
     for (int b = 0; b < p.B; ++b) {
       for (int h = 0; h < p.H; ++h) {
         const uint16_t* xp = p.x + b * p.xs_b + h * p.xs_h + srow * p.xs_s + c * 8;
-        const u32x4 x = *reinterpret_cast<const u32x4*>(xp);
+        const u32x4 x = load_once(reinterpret_cast<const u32x4*>(xp));
         const u32x4 y = p.out_f16 ? rotate4_bf16<true>(x, cs, sn) : rotate4_bf16<false>(x, cs, sn);
         uint16_t* yp = static_cast<uint16_t*>(p.y) + b * p.ys_b + h * p.ys_h + srow * p.ys_s + c * 8;
         *reinterpret_cast<u32x4*>(yp) = y;
