@@ -502,8 +502,9 @@ def main():
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default 10; 1 for the chunked workload)")
     ap.add_argument("--warmup", type=int, default=None, help="warm-up steps (default 3; 1 for the chunked workload)")
     ap.add_argument("--workload", default="llama3_70b_128k_dynntk")
-    ap.add_argument("--k-mode", choices=["prerotate", "fused"], default="prerotate",
-                    help="K rotated once by lcx_rope_apply_qk (default) or inside the attention tile load")
+    ap.add_argument("--k-mode", choices=["prerotate", "fused", "precise"], default="prerotate",
+                    help="K rotated once by lcx_rope_apply_qk (default), inside the attention tile load, or "
+                         "inside the tile load with the precise QK^T form (f16 high/low parts, three products)")
     ap.add_argument("--v-layout", choices=["tiles", "rows"], default="tiles",
                     help="V packed into 64-key tiles by lcx_attn_pack_v inside the step (default) or read as rows")
     ap.add_argument("--cpu-rows", type=int, default=None,
@@ -582,7 +583,7 @@ def main():
         if ev: ev[3].record(stream)
         lcx.attn_fwd(q, k_rot if args.k_mode == "prerotate" else k, vv, o, lse, rope_q=True,
                      rope_k=args.k_mode != "prerotate", cos=cos, sin=sin, rope=cfg,
-                     window=w.window, n_sink=w.n_sink)
+                     window=w.window, n_sink=w.n_sink, precise_qk=args.k_mode == "precise")
         if ev: ev[4].record(stream)
 
     for _ in range(args.warmup):
@@ -652,7 +653,8 @@ def main():
                    "head_dim": w.d, "seq_len": w.n, "rope": w.scheme, "rope_base": w.base,
                    "L_train": w.L_train, "cur_len": w.cur_len, "causal": True,
                    "k_rope": args.k_mode, "v_layout": args.v_layout,
-                   "mfma": ("QK^T f16 operands, PV " + ("f16" if args.v_layout == "tiles" else "bf16")
+                   "mfma": (("QK^T as three f16 products of high/low parts" if args.k_mode == "precise"
+                             else "QK^T f16 operands") + ", PV " + ("f16" if args.v_layout == "tiles" else "bf16")
                             + " operands, fp32 accumulate")},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "tokens_per_s": round(tokens / (ms_step * 1e-3), 1),

@@ -145,6 +145,14 @@ typedef struct {
   int32_t accumulate;       /* 1: merge into the existing (o f32, lse) in the epilogue */
   int32_t v_tiled;          /* 1: v is in the tile layout of lcx_attn_pack_v; v_strides[0..1]
                                are its batch and head strides (elements), v_strides[2] unused */
+  int32_t precise_qk;       /* 1: QK^T from f16 high and low parts of the rotated, scaled q and
+                               of the rotated k (three products: hi·hi + hi·lo + lo·hi), which
+                               removes their f16 rounding from the logits (relative error
+                               ~2^-22 instead of 2^-11) for inputs with large logits.
+                               Needs rope_k = 1 (k raw bf16, rotated in the kernel: a
+                               pre-rotated k has already been rounded); 2.1-2.2 times the
+                               time of the default.  0: one product on operands rounded
+                               once to f16. */
 } lcx_attn_args;
 
 /*
@@ -161,8 +169,9 @@ typedef struct {
  * Errors: INVALID_ARG for NULL q/k/v/o/lse, sizes <= 0 (n_kv may be 0: all
  * rows empty), Hq % Hkv != 0, window < -1, n_sink < 0, rope_q/rope_k not 0/1,
  * rope_q or rope_k without rope, rope->head_dim != d, tables missing or not
- * covering the rotated positions, accumulate with a bf16 o, f16 with rope on;
- * UNSUPPORTED for d not 64/128, causal == 0, non-16-byte-aligned rows.
+ * covering the rotated positions, accumulate with a bf16 o, f16 with rope on,
+ * precise_qk not 0/1; UNSUPPORTED for d not 64/128, causal == 0,
+ * non-16-byte-aligned rows, precise_qk without rope_k.
  */
 lcx_status lcx_attn_fwd(const lcx_attn_args* a, hipStream_t stream);
 
@@ -185,7 +194,7 @@ lcx_status lcx_attn_fwd(const lcx_attn_args* a, hipStream_t stream);
  *             [n_splits][B][Hq][n_q]: caller-owned workspace, overwritten.
  * Errors: as lcx_attn_fwd, plus INVALID_ARG for n_splits out of range, a NULL
  * workspace or accumulate = 1; UNSUPPORTED for n_q > 8, (Hq/Hkv)·n_q > 64, K
- * not pre-rotated f16, B or Hkv > 65535.
+ * not pre-rotated f16, precise_qk = 1, B or Hkv > 65535.
  */
 lcx_status lcx_attn_decode(const lcx_attn_args* a, int32_t n_splits, float* o_part, float* lse_part,
                            hipStream_t stream);

@@ -46,7 +46,7 @@ class AttnArgs(ctypes.Structure):
                 ("cos_tab", _vp), ("sin_tab", _vp), ("tab_pos0", _i64), ("tab_len", _i64),
                 ("rope", ctypes.POINTER(RopeCfg)), ("softmax_scale", _f32), ("causal", _i32),
                 ("window", _i64), ("n_sink", _i32), ("o", _vp), ("o_dtype", _i32),
-                ("lse", _vp), ("accumulate", _i32), ("v_tiled", _i32)]
+                ("lse", _vp), ("accumulate", _i32), ("v_tiled", _i32), ("precise_qk", _i32)]
 
 
 class BwdArgs(ctypes.Structure):
@@ -200,7 +200,7 @@ def _workspace(t, name, shape):
 
 
 def _attn_args(q, k, v, o, lse, *, rope_q, rope_k, cos, sin, tab_pos0, cfg, softmax_scale,
-               window, n_sink, q_pos0, k_pos0, accumulate, causal=True):
+               window, n_sink, q_pos0, k_pos0, accumulate, causal=True, precise_qk=False):
     _rows4(q, "q", dtypes=(torch.bfloat16, torch.float16))
     B, Hq, n_q, d = q.shape
     _rows4(k, "k", dtypes=(torch.bfloat16, torch.float16))
@@ -247,6 +247,7 @@ def _attn_args(q, k, v, o, lse, *, rope_q, rope_k, cos, sin, tab_pos0, cfg, soft
     a.o, a.o_dtype = o.data_ptr(), _DT[o.dtype]
     a.lse = lse.data_ptr()
     a.accumulate = int(accumulate)
+    a.precise_qk = int(precise_qk)
     return a
 
 
@@ -266,9 +267,10 @@ def pack_v(v, out=None):
 
 def attn_fwd(q, k, v, o=None, lse=None, *, rope_q=False, rope_k=False, cos=None, sin=None,
              tab_pos0=0, rope=None, softmax_scale=0.0, window=-1, n_sink=0, q_pos0=0, k_pos0=0,
-             accumulate=False, out_dtype=torch.bfloat16, causal=True):
+             accumulate=False, out_dtype=torch.bfloat16, causal=True, precise_qk=False):
     """lcx_attn_fwd.  q [B,Hq,n_q,d], k [B,Hkv,n_kv,d], v [B,Hkv,n_kv,d] or its pack_v
-    tile layout.  Returns (o, lse)."""
+    tile layout.  precise_qk (with rope_k): QK^T from f16 high/low parts of the rotated
+    operands.  Returns (o, lse)."""
     B, Hq, n_q, d = q.shape
     if o is None:
         o = torch.empty((B, Hq, n_q, d), dtype=out_dtype, device=q.device)
@@ -277,7 +279,7 @@ def attn_fwd(q, k, v, o=None, lse=None, *, rope_q=False, rope_k=False, cos=None,
     a = _attn_args(q, k, v, o, lse, rope_q=rope_q, rope_k=rope_k, cos=cos, sin=sin,
                    tab_pos0=tab_pos0, cfg=rope, softmax_scale=softmax_scale, window=window,
                    n_sink=n_sink, q_pos0=q_pos0, k_pos0=k_pos0, accumulate=accumulate,
-                   causal=causal)
+                   causal=causal, precise_qk=precise_qk)
     _check(_lib.lcx_attn_fwd(ctypes.byref(a), _stream(q)))
     return o, lse
 

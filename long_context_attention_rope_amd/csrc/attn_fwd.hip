@@ -114,6 +114,62 @@ __device__ __forceinline__ void load_q(const AttnParams& p, const uint16_t* qbas
 }
 
 
+// f16 high and low parts of a pair of fp32 values: hi = f16(x), lo =
+// f16(x - hi) (x - hi is exact in fp32; the f16 MFMA takes lo's subnormal
+// values as they are)
+struct F16Split {
+  uint32_t hi, lo;
+};
+__device__ __forceinline__ F16Split split_f16x2(float a, float b) {
+  const uint32_t hi = pack_f16x2(a, b);
+  return {hi, pack_f16x2(a - f16lo(hi), b - f16hi(hi))};
+}
+
+// load_q for the precise QK^T form: the rotated, scaled q as f16 high (qh)
+// and low (ql) parts
+template <int D>
+__device__ __forceinline__ void load_q_split(const AttnParams& p, const uint16_t* qbase, int64_t qi,
+                                             int h2, f16x8 (&qh)[D / 16], f16x8 (&ql)[D / 16]) {
+  const bool valid = qi < p.n_q;
+  const int64_t trow = p.q_pos0 + qi - p.tab_pos0;
+  const float sc = p.scale_log2;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    const int col = 16 * c + 8 * h2;
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (valid) raw = *reinterpret_cast<const u32x4*>(qbase + qi * p.qs_s + col);
+    float x[8];
+    if (p.q_mode == 2) {
+      f32x4 cs = {1.f, 1.f, 1.f, 1.f}, sn = {0.f, 0.f, 0.f, 0.f};
+      if (valid) {
+        cs = *reinterpret_cast<const f32x4*>(p.cos_tab + trow * (D / 2) + col / 2);
+        sn = *reinterpret_cast<const f32x4*>(p.sin_tab + trow * (D / 2) + col / 2);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x0 = bf16lo(raw[i]), x1 = bf16hi(raw[i]);
+        x[2 * i] = (x0 * cs[i] - x1 * sn[i]) * sc;
+        x[2 * i + 1] = (x0 * sn[i] + x1 * cs[i]) * sc;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = (p.q_mode == 1 ? bf16lo(raw[i]) : f16lo(raw[i])) * sc;
+        x[2 * i + 1] = (p.q_mode == 1 ? bf16hi(raw[i]) : f16hi(raw[i])) * sc;
+      }
+    }
+    u32x4 wh, wl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const F16Split sp = split_f16x2(x[2 * i], x[2 * i + 1]);
+      wh[i] = sp.hi;
+      wl[i] = sp.lo;
+    }
+    qh[c] = __builtin_bit_cast(f16x8, wh);
+    ql[c] = __builtin_bit_cast(f16x8, wl);
+  }
+}
+
 // Tile copy global -> LDS with no register round trip: per wave LPW buffer
 // loads of 64 lanes x 16 bytes, each filling RPL consecutive LDS rows; lane L
 // of load i fills row r = (wave·LPW + i)·RPL + L / CPR, slot L % CPR, with
@@ -258,6 +314,24 @@ struct KRegStage {
       *reinterpret_cast<u32x4*>(ks + lds_off[i]) = w;
     }
   }
+  // precise QK^T form (KMODE 2): the rotated k as f16 high parts into ks and
+  // low parts into kls (the same layout)
+  __device__ __forceinline__ void store_split(uint16_t* ks, uint16_t* kls) const {
+    static_assert(KMODE == 2, "the split is of the kernel's own rotation");
+#pragma unroll
+    for (int i = 0; i < T::KCH; ++i) {
+      u32x4 wh, wl;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x0 = bf16lo(reg[i][j]), x1 = bf16hi(reg[i][j]);
+        const F16Split sp = split_f16x2(x0 * cs[i][j] - x1 * sn[i][j], x0 * sn[i][j] + x1 * cs[i][j]);
+        wh[j] = sp.hi;
+        wl[j] = sp.lo;
+      }
+      *reinterpret_cast<u32x4*>(ks + lds_off[i]) = wh;
+      *reinterpret_cast<u32x4*>(kls + lds_off[i]) = wl;
+    }
+  }
 };
 
 // S^T = K·Q^T - m for NB 32-key blocks of a tile from block kb0 on: lane
@@ -279,6 +353,26 @@ __device__ __forceinline__ void qk_tile(const uint16_t* ks, const int (&koff)[D 
   // keep four operand reads in flight ahead of the products (left to
   // itself the scheduler issues each read one product ahead and waits on it)
   pipeline_reads<(D / 16) * NB, 1, 4, 0>();
+}
+
+// qk_tile in the precise form: S^T = Kh·Qh^T + Kh·Ql^T + Kl·Qh^T - m over
+// both 32-key blocks (the high and low f16 parts of k in ks and kls, of q in
+// qh and ql; the lo·lo term, ~2^-22 relative, is left out)
+template <int D>
+__device__ __forceinline__ void qk_tile_precise(const uint16_t* ks, const uint16_t* kls, const int (&koff)[D / 16],
+                                                const f16x8 (&qh)[D / 16], const f16x8 (&ql)[D / 16],
+                                                const f32x16& init, f32x16 (&s)[2]) {
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const f16x8 ah = *reinterpret_cast<const f16x8*>(ks + kb * 32 * D + koff[c]);
+      const f16x8 al = *reinterpret_cast<const f16x8*>(kls + kb * 32 * D + koff[c]);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, qh[c], c == 0 ? init : s[kb], 0, 0, 0);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, ql[c], s[kb], 0, 0, 0);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, qh[c], s[kb], 0, 0, 0);
+    }
+  }
 }
 
 // A operand of O^T += V^T·P^T for d-block db and 16-key chunk kc.  Lane l
@@ -598,8 +692,9 @@ __device__ __forceinline__ void operand_offsets(int lane, int (&koff)[D / 16], i
   }
 }
 
-template <int D, int KMODE, int NW, bool VT>
+template <int D, int KMODE, int NW, bool VT, bool PRECISE = false>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnParams p) {
+  static_assert(!PRECISE || KMODE == 2, "the precise QK^T form splits the kernel's own rotation of k");
   using T = Tile<D, NW>;
   // Stages of (K, V) tiles in LDS, one array each so that every unrolled step
   // names its stages directly.  Pre-rotated f16 K and V are copied straight
@@ -609,6 +704,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
   constexpr int E3 = NST > 2 ? T::ELEMS : 8;
   __shared__ __attribute__((aligned(1024))) uint16_t k_st0[T::ELEMS], k_st1[T::ELEMS], k_st2[E3];
   __shared__ __attribute__((aligned(1024))) uint16_t v_st0[T::ELEMS], v_st1[T::ELEMS], v_st2[E3];
+  // low parts of K (precise QK^T form)
+  constexpr int EL = PRECISE ? T::ELEMS : 8;
+  __shared__ __attribute__((aligned(1024))) uint16_t kl_st0[EL], kl_st1[EL];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -626,9 +724,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
   // no 16 registers to spare
   Rows32<D, VT, D == 64 || (KMODE == 0 && VT)> rows;
   rows.init(p, bt.row0 + wave * 32, l32);
-  // Q fragment (RoPE fused here when q_mode == 2)
-  f16x8 qf[D / 16];
-  load_q<D>(p, qbase, rows.qi, h2, qf);
+  // Q fragment (RoPE fused here when q_mode == 2); its low part in the
+  // precise form
+  f16x8 qf[D / 16], qlo[PRECISE ? D / 16 : 1];
+  if constexpr (PRECISE)
+    load_q_split<D>(p, qbase, rows.qi, h2, qf, qlo);
+  else
+    load_q<D>(p, qbase, rows.qi, h2, qf);
 
   // ---- staging and per-lane LDS read offsets
   LdsCopy<D, NW, true> kcp;
@@ -659,8 +761,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     else
       vcp.issue(vs, j0);
   };
+  // kls, kls_next: the low parts of K (precise form, two stages)
   auto step = [&](const uint16_t* ks, const uint16_t* vs, uint16_t* ks_next, uint16_t* vs_next,
-                  int t) {
+                  const uint16_t* kls, uint16_t* kls_next, int t) {
     const int tn = t + NST - 1;
     const bool pre = tn < ntl;
     if (pre) {
@@ -668,13 +771,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
       issue(ks_next, vs_next, tn);
     }
     f32x16 s_cur[2];
-    qk_tile<D>(ks, koff, qf, rows.qk_init(), s_cur);
+    if constexpr (PRECISE)
+      qk_tile_precise<D>(ks, kls, koff, qf, qlo, rows.qk_init(), s_cur);
+    else
+      qk_tile<D>(ks, koff, qf, rows.qk_init(), s_cur);
     rows.mask(p, s_cur, bt.j0(t), h2);
     rows.rescale(rows.tile_max(s_cur), s_cur);
     u32x4 pf[4];
     rows.probs(s_cur, pf);
     pv_tile<D, VT>(vs, voff, pf, rows.oacc);
-    if constexpr (KMODE != 0) {
+    if constexpr (PRECISE) {
+      if (pre) kreg.store_split(ks_next, kls_next);
+    } else if constexpr (KMODE != 0) {
       if (pre) kreg.store(ks_next);
     }
     if (NST > 2 && pre)
@@ -686,7 +794,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
   if (ntl > 0) {
     if constexpr (KMODE != 0) {
       kreg.load(bt.j0(0));
-      kreg.store(k_st0);
+      if constexpr (PRECISE)
+        kreg.store_split(k_st0, kl_st0);
+      else
+        kreg.store(k_st0);
     }
     issue(k_st0, v_st0, 0);
   }
@@ -696,15 +807,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
   stage_barrier<0>();
   for (int t = 0; t < ntl; t += NST) {
     if constexpr (NST > 2) {
-      step(k_st0, v_st0, k_st2, v_st2, t);
+      step(k_st0, v_st0, k_st2, v_st2, kl_st0, kl_st1, t);
       if (t + 1 >= ntl) break;
-      step(k_st1, v_st1, k_st0, v_st0, t + 1);
+      step(k_st1, v_st1, k_st0, v_st0, kl_st0, kl_st1, t + 1);
       if (t + 2 >= ntl) break;
-      step(k_st2, v_st2, k_st1, v_st1, t + 2);
+      step(k_st2, v_st2, k_st1, v_st1, kl_st0, kl_st1, t + 2);
     } else {
-      step(k_st0, v_st0, k_st1, v_st1, t);
+      step(k_st0, v_st0, k_st1, v_st1, kl_st0, kl_st1, t);
       if (t + 1 >= ntl) break;
-      step(k_st1, v_st1, k_st0, v_st0, t + 1);
+      step(k_st1, v_st1, k_st0, v_st0, kl_st1, kl_st0, t + 1);
     }
   }
 
@@ -861,7 +972,9 @@ __global__ __launch_bounds__(64 * NW) void attn_decode_kernel(const AttnParams p
   template __global__ void attn_fwd_kernel<D, 2, NW, false>(const AttnParams);    \
   template __global__ void attn_fwd_kernel<D, 0, NW, true>(const AttnParams);     \
   template __global__ void attn_fwd_kernel<D, 1, NW, true>(const AttnParams);     \
-  template __global__ void attn_fwd_kernel<D, 2, NW, true>(const AttnParams);
+  template __global__ void attn_fwd_kernel<D, 2, NW, true>(const AttnParams);     \
+  template __global__ void attn_fwd_kernel<D, 2, NW, false, true>(const AttnParams); \
+  template __global__ void attn_fwd_kernel<D, 2, NW, true, true>(const AttnParams);
 LCX_ATTN_INST(64, kNWd64)
 LCX_ATTN_INST(128, kNWd128)
 #undef LCX_ATTN_INST
@@ -880,7 +993,12 @@ hipError_t launch_dv(const AttnParams& p, hipStream_t s, unsigned grid) {
   switch (p.k_mode) {
     case 0: hipLaunchKernelGGL((attn_fwd_kernel<D, 0, NW, VT>), dim3(grid), block, 0, s, p); break;
     case 1: hipLaunchKernelGGL((attn_fwd_kernel<D, 1, NW, VT>), dim3(grid), block, 0, s, p); break;
-    default: hipLaunchKernelGGL((attn_fwd_kernel<D, 2, NW, VT>), dim3(grid), block, 0, s, p); break;
+    default:
+      if (p.precise_qk)
+        hipLaunchKernelGGL((attn_fwd_kernel<D, 2, NW, VT, true>), dim3(grid), block, 0, s, p);
+      else
+        hipLaunchKernelGGL((attn_fwd_kernel<D, 2, NW, VT>), dim3(grid), block, 0, s, p);
+      break;
   }
   return hipGetLastError();
 }

@@ -167,6 +167,11 @@ lcx_status check_attn(const lcx_attn_args* a, bool chunked) {
   if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
     return fail(LCX_ERR_UNSUPPORTED, "q, k, v, o must be 16-byte aligned");
   if (a->v_tiled != 0 && a->v_tiled != 1) return fail(LCX_ERR_INVALID_ARG, "v_tiled must be 0 or 1");
+  if (a->precise_qk != 0 && a->precise_qk != 1) return fail(LCX_ERR_INVALID_ARG, "precise_qk must be 0 or 1");
+  // the high/low split is taken from the kernel's own rotation of raw k; a
+  // pre-rotated k has already been rounded
+  if (a->precise_qk && !a->rope_k)
+    return fail(LCX_ERR_UNSUPPORTED, "precise_qk needs raw bf16 k rotated in the kernel (rope_k = 1)");
   // tile layout: only the batch and head strides are used
   const int64_t v_st[3] = {a->v_strides[0], a->v_strides[1], a->v_tiled ? 8 : a->v_strides[2]};
   if (!strides_ok(a->q_strides, 8) || !strides_ok(a->k_strides, 8) || !strides_ok(v_st, 8))
@@ -218,6 +223,7 @@ lcx::AttnParams make_params(const lcx_attn_args* a) {
   p.o_mode = a->o_dtype == LCX_BF16 ? 0 : (a->accumulate ? 2 : 1);
   p.causal = a->causal;
   p.v_tiled = a->v_tiled;
+  p.precise_qk = a->precise_qk;
   return p;
 }
 
@@ -326,6 +332,7 @@ lcx_status check_decode(const lcx_attn_args* a, int32_t n_splits) {
     return fail(LCX_ERR_UNSUPPORTED, "decode needs (Hq/Hkv)·n_q <= 64");
   if (a->rope_k || a->k_dtype != LCX_F16)
     return fail(LCX_ERR_UNSUPPORTED, "decode reads a pre-rotated f16 K cache (rope_k = 0, k_dtype F16)");
+  if (a->precise_qk) return fail(LCX_ERR_UNSUPPORTED, "decode has no precise_qk form");
   if (n_splits < 1 || n_splits > 65535) return fail(LCX_ERR_INVALID_ARG, "n_splits %d outside 1..65535", n_splits);
   if (a->B > 65535 || a->Hkv > 65535) return fail(LCX_ERR_UNSUPPORTED, "B and Hkv must be <= 65535");
   return LCX_OK;

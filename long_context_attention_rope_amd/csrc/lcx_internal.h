@@ -57,6 +57,7 @@ struct AttnParams {
   int32_t xcd_map; // 1: XCD-aware block order
   int32_t causal;
   int32_t v_tiled;  // 1: v in the 64-key tile layout (vs_b, vs_h its strides)
+  int32_t precise_qk;  // 1: QK^T from f16 high/low parts of q~ and k~ (k_mode 2 only)
 };
 
 // backward pass (gradients of the attention rows)

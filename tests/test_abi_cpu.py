@@ -156,6 +156,8 @@ ATTN_BAD = [
     (1, dict(accumulate=1)), (1, dict(o_dtype=7)), (1, dict(softmax_scale=-1.0)),
     (2, dict(q=FAKE + 2)), (2, dict(q_strides=(ctypes.c_int64 * 3)(0, 0, 60))),
     (1, dict(v_tiled=2)), (2, dict(v_tiled=1, v_strides=(ctypes.c_int64 * 3)(12, 16384, 0))),
+    # precise QK^T: 0 or 1, and only on the kernel's own rotation of raw k
+    (1, dict(precise_qk=2)), (2, dict(precise_qk=1)), (2, dict(precise_qk=1, k_dtype=2)),
 ]
 
 
@@ -191,6 +193,7 @@ def test_decode_rejects(lcx):
     assert f(ctypes.byref(_args(lcx, n_q=4)), 8, FAKE, FAKE, None) == 2          # bf16 K
     assert f(ctypes.byref(_args(lcx, n_q=4, k_dtype=lcx.F16, o_dtype=lcx.F32, accumulate=1)),
              8, FAKE, FAKE, None) == 1
+    assert f(ctypes.byref(_args(lcx, n_q=4, k_dtype=lcx.F16, precise_qk=1)), 8, FAKE, FAKE, None) == 2
 
 
 def _bwd_args(lcx, **kw):

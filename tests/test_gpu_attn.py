@@ -34,10 +34,11 @@ def _run(lcx, w, q, k, v, *, k_mode="pre_f16", out_dtype=torch.bfloat16, q_pos0=
     cfg = _cfg(lcx, w)
     n_tab = tab_n or max(q_pos0 + q.shape[2], k_pos0 + k.shape[2])
     cos, sin = lcx.rope_tables(cfg, n_tab, device=U.dev())
-    if k_mode == "fused":
+    if k_mode in ("fused", "precise"):
+        # "precise": QK^T from f16 high/low parts of the kernel's own rotation
         o, lse = lcx.attn_fwd(qd, kd, vd, rope_q=True, rope_k=True, cos=cos, sin=sin, rope=cfg,
                               window=w.window, n_sink=w.n_sink, q_pos0=q_pos0, k_pos0=k_pos0,
-                              out_dtype=out_dtype)
+                              out_dtype=out_dtype, precise_qk=(k_mode == "precise"))
     else:
         odt = torch.float16 if k_mode == "pre_f16" else torch.bfloat16
         _, kr = lcx.rope_apply_qk(None, kd, cos, sin, pos0=k_pos0, out_dtype=odt)
@@ -124,7 +125,8 @@ def test_small_shapes_full(lcx, name, Hq, Hkv, d, n, scheme, window, n_sink, B):
                    factors=_pair_factors(d, n) if scheme == "pair_factors" else None)
     q, k, v = U.inputs(w)
     o_ref, l_ref = _all(w, q, k, v)
-    for k_mode, v_tiled in (("pre_f16", False), ("pre_f16", True), ("fused", False), ("fused", True)):
+    for k_mode, v_tiled in (("pre_f16", False), ("pre_f16", True), ("fused", False), ("fused", True),
+                            ("precise", False), ("precise", True)):
         o, lse = _run(lcx, w, q, k, v, k_mode=k_mode, v_tiled=v_tiled)
         U.check(o.float().cpu().numpy().reshape(-1, d), lse.cpu().numpy().reshape(-1), o_ref, l_ref,
                 f"{name}/{k_mode}/{'tiles' if v_tiled else 'rows'}")
@@ -173,7 +175,8 @@ def test_peaky_softmax_exercises_rescaling(lcx):
     # moves by at most the largest such move over the row's kept keys, plus u
     # from the row sums of P rounded to f16 (and 1e-4 for the fp32 tables,
     # rotation and accumulation, each far smaller).  That per-row bound is
-    # asserted.
+    # asserted.  The precise QK^T form (next test) meets the stated bar on the
+    # same input.
     w = W.TINY.with_(n=600, seed=9)
     q, k, v = U.inputs(w)
     qf = (q.astype(np.uint32) << 16).view(np.float32) * 8.0
@@ -203,6 +206,27 @@ def test_peaky_softmax_exercises_rescaling(lcx):
           f"(stated bar 1e-3 exceeded on {over} of {el.size} rows); derived bound: median "
           f"{np.median(bound):.3e}, max {bound.max():.3e}, tightest ratio {(el / bound).max():.3f}")
     assert np.all(el <= bound), f"LSE beyond the f16 rounding bound on {int((el > bound).sum())} rows"
+
+
+@pytest.mark.parametrize("v_tiled", [False, True], ids=["v_rows", "v_tiles"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_peaky_softmax_precise_qk_meets_the_stated_bar(lcx, d, v_tiled):
+    # the same stress input (q x 8, logits ~ N(0, 64)) through the precise
+    # QK^T form: with the f16 rounding of q~ and k~ taken out of the logits,
+    # the stated LSE bar (1e-3) holds again (what remains: the row sums of P
+    # rounded to f16, <= 2^-11 relative, and fp32 arithmetic)
+    w = W.TINY.with_(n=600, seed=9, d=d, base=10000.0 if d == 64 else 500000.0)
+    q, k, v = U.inputs(w)
+    qf = (q.astype(np.uint32) << 16).view(np.float32) * 8.0
+    q8 = (qf.view(np.uint32) >> 16).astype(np.uint16)
+    o_ref, l_ref = _all(w, q8, k, v)
+    o, lse = _run(lcx, w, q8, k, v, k_mode="precise", v_tiled=v_tiled)
+    U.check(o.float().cpu().numpy().reshape(-1, w.d), lse.cpu().numpy().reshape(-1), o_ref, l_ref,
+            f"peaky/precise/d{d}/{'tiles' if v_tiled else 'rows'}")
+    # the default form on the same input, for the log: its LSE error follows the logit scale
+    o1, l1 = _run(lcx, w, q8, k, v, k_mode="fused", v_tiled=v_tiled)
+    U.log(f"peaky d{d}: LSE max-abs precise {np.abs(lse.cpu().numpy().reshape(-1) - l_ref).max():.3e}, "
+          f"default {np.abs(l1.cpu().numpy().reshape(-1) - l_ref).max():.3e}")
 
 
 def test_deterministic_and_every_output_written(lcx):
