@@ -586,17 +586,22 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
     const int hi = clamp_i32(qpos_t - kpos);  // causal: row off kept iff hi + off >= 0
     const int lo = p.window >= 0 ? clamp_i32(qpos_t - kpos - p.window) : -(1 << 30);  // lo + off <= 0
     const int rrem = clamp_tile(p.n_q - j0);
+    // S and dP of both 32-row halves first, then the masks (one branch), then
+    // per half the softmax and the dV/dK products: the second half's products
+    // are in flight while the first half's softmax runs, and the softmax of
+    // the second half can overlap the first half's dV/dK products
+    f32x4 sc[2][2], dp[2][2];  // [half kc][row block u]
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      // S, dP for row blocks 2kc, 2kc+1
-      f32x4 sc[2], dp[2];
+    for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          sc[u][r] = 0.f;
-          dp[u][r] = 0.f;
+          sc[kc][u][r] = 0.f;
+          dp[kc][u][r] = 0.f;
         }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
       for (int c = 0; c < D / 32; ++c)
 #pragma unroll
@@ -604,20 +609,24 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
           const int rb = 2 * kc + u;
           const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qs + rb * 16 * D + roff[c]);
           const bf16x8 ag = *reinterpret_cast<const bf16x8*>(gs + rb * 16 * D + roff[c]);
-          sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, kf[c], sc[u], 0, 0, 0);
-          dp[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, vf[c], dp[u], 0, 0, 0);
+          sc[kc][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, kf[c], sc[kc][u], 0, 0, 0);
+          dp[kc][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, vf[c], dp[kc][u], 0, 0, 0);
         }
-      // element (u, r) is row 32kc + 16u + 4g + r of the tile and the lane's key
-      if (!all_kept) {
+    // element (kc, u, r) is row 32kc + 16u + 4g + r of the tile and the lane's key
+    if (!all_kept) {
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int off = 32 * kc + 16 * u + 4 * g + r;
             const bool ok = kvalid & (off < rrem) & (!p.causal | (hi + off >= 0)) & ((lo + off <= 0) | k_sink);
-            sc[u][r] = ok ? sc[u][r] : -INFINITY;
+            sc[kc][u][r] = ok ? sc[kc][u][r] : -INFINITY;
           }
-      }
+    }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
       // P = exp2(S·sigma·log2 e - LSE·log2 e), dS = P (dP - D)
       u32x4 wp, wd;
 #pragma unroll
@@ -630,8 +639,8 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
         float pr[4], ds[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][r], p.scale_log2, -l2[r]));
-          ds[r] = pr[r] * (dp[u][r] - dd[r]);
+          pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kc][u][r], p.scale_log2, -l2[r]));
+          ds[r] = pr[r] * (dp[kc][u][r] - dd[r]);
         }
         wp[2 * u] = pack_bf16x2(pr[0], pr[1]);
         wp[2 * u + 1] = pack_bf16x2(pr[2], pr[3]);
