@@ -55,6 +55,28 @@ def test_full_size_sampled(lcx, w):
     assert torch.isfinite(o.float()).all().item()
 
 
+@pytest.mark.timeout(600)
+def test_full_size_sampled_precise_qk(lcx):
+    # the precise QK^T form (f16 high/low parts of the kernel's own rotation of
+    # raw k) at the Llama-3-8B-shaped YaRN layer's full size, on the same
+    # sampled rows, held to the stated bar
+    w = W.LLAMA8B_32K
+    q, k, v = U.inputs(w)
+    qd, kd, vd = U.to_dev(q), U.to_dev(k), U.to_dev(v)
+    cfg = lcx.rope_cfg(w.scheme, w.base, w.d, w.L_train, w.L_target, w.cur_len, w.alpha, w.beta)
+    cos, sin = lcx.rope_tables(cfg, w.n, device=U.dev())
+    o, lse = lcx.attn_fwd(qd, kd, lcx.pack_v(vd), rope_q=True, rope_k=True, cos=cos, sin=sin, rope=cfg,
+                          precise_qk=True)
+    torch.cuda.synchronize()
+    bb, hh, rr = U.sample_rows(w, 4096, seed=w.seed)
+    idx = [torch.from_numpy(a.astype(np.int64)).to(U.dev()) for a in (bb, hh, rr)]
+    o_s = o[idx[0], idx[1], idx[2]].float().cpu().numpy()
+    l_s = lse[idx[0], idx[1], idx[2]].cpu().numpy()
+    o_ref, l_ref = U.oracle_rows(w, q, k, v, bb, hh, rr)
+    U.check(o_s, l_s, o_ref, l_ref, w.name + "/precise")
+    assert torch.isfinite(lse).all().item() and torch.isfinite(o.float()).all().item()
+
+
 @pytest.mark.timeout(900)
 def test_million_token_chunked_sampled(lcx):
     w = W.MILLION
