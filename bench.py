@@ -205,6 +205,8 @@ def bench_chunked(args, w):
     o = torch.empty((w.B, w.Hq, w.n, w.d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.B, w.Hq, w.n), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    sched = torch.empty(lcx.SCHED_BYTES // 8, dtype=torch.int64, device=dev) \
+        if args.work_order == "dynamic" else False
 
     def step(ev=None, o_part=None, lse_part=None):
         if ev: ev[0].record(stream)
@@ -213,7 +215,7 @@ def bench_chunked(args, w):
         lcx.pack_v(v, out=v_tiles)
         if ev: ev[1].record(stream)
         lcx.attn_fwd_chunked(q, k_rot, v_tiles, w.chunk, acc_o, acc_l, o, lse, o_part=o_part,
-                             lse_part=lse_part, rope_q=True, cos=cos, sin=sin, rope=cfg)
+                             lse_part=lse_part, rope_q=True, cos=cos, sin=sin, rope=cfg, sched=sched)
         if ev: ev[2].record(stream)
 
     for _ in range(args.warmup):
@@ -255,7 +257,8 @@ def bench_chunked(args, w):
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
                    "seq_len": w.n, "rope": w.scheme, "rope_base": w.base, "L_train": w.L_train,
                    "L_target": w.L_target, "causal": True, "kv_chunk": w.chunk, "chunks": n_chunks,
-                   "merge": "fused into each chunk's epilogue (accumulate)", "v_layout": "tiles"},
+                   "merge": "fused into each chunk's epilogue (accumulate)", "v_layout": "tiles",
+                   "work_order": args.work_order},
         "pct_bf16_peak": round(100 * flop / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "tokens_per_s": round(w.B * w.n / (ms_step * 1e-3), 1),
         "kernels_ms": {"tables_rotate_pack": round(prep_ms, 3), "chunked_attention_fused_merge": round(drv_ms, 1),
@@ -505,6 +508,9 @@ def main():
     ap.add_argument("--k-mode", choices=["prerotate", "fused", "precise"], default="prerotate",
                     help="K rotated once by lcx_rope_apply_qk (default), inside the attention tile load, or "
                          "inside the tile load with the precise QK^T form (f16 high/low parts, three products)")
+    ap.add_argument("--work-order", choices=["dynamic", "static"], default="dynamic",
+                    help="forward work order: per-XCD queues with stealing (lcx_attn_args.sched), "
+                         "or one fixed unit per workgroup")
     ap.add_argument("--v-layout", choices=["tiles", "rows"], default="tiles",
                     help="V packed into 64-key tiles by lcx_attn_pack_v inside the step (default) or read as rows")
     ap.add_argument("--cpu-rows", type=int, default=None,
@@ -571,6 +577,8 @@ def main():
     o = torch.empty((w.B, w.Hq, w.n, w.d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.B, w.Hq, w.n), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    sched = torch.empty(lcx.SCHED_BYTES // 8, dtype=torch.int64, device=dev) \
+        if args.work_order == "dynamic" else False
 
     def step(ev=None):
         if ev: ev[0].record(stream)
@@ -583,7 +591,8 @@ def main():
         if ev: ev[3].record(stream)
         lcx.attn_fwd(q, k_rot if args.k_mode == "prerotate" else k, vv, o, lse, rope_q=True,
                      rope_k=args.k_mode != "prerotate", cos=cos, sin=sin, rope=cfg,
-                     window=w.window, n_sink=w.n_sink, precise_qk=args.k_mode == "precise")
+                     window=w.window, n_sink=w.n_sink, precise_qk=args.k_mode == "precise",
+                     sched=sched)
         if ev: ev[4].record(stream)
 
     for _ in range(args.warmup):
@@ -628,7 +637,8 @@ def main():
     value = flop / (ms_step * 1e-3) / 1e12
     attn_tflops = flop / (attn_ms * 1e-3) / 1e12
     # the committed counter runs cover the default configuration of the 70B layer only
-    profiled = w.name == W.LLAMA70B_128K.name and args.k_mode == "prerotate" and args.v_layout == "tiles"
+    profiled = w.name == W.LLAMA70B_128K.name and args.k_mode == "prerotate" and args.v_layout == "tiles" \
+        and args.work_order == "dynamic"
     traffic = traffic_from_profile(flop) if profiled else None
 
     tab_bytes = w.n * half * 8
@@ -652,7 +662,7 @@ def main():
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "head_dim": w.d, "seq_len": w.n, "rope": w.scheme, "rope_base": w.base,
                    "L_train": w.L_train, "cur_len": w.cur_len, "causal": True,
-                   "k_rope": args.k_mode, "v_layout": args.v_layout,
+                   "k_rope": args.k_mode, "v_layout": args.v_layout, "work_order": args.work_order,
                    "mfma": (("QK^T as three f16 products of high/low parts" if args.k_mode == "precise"
                              else "QK^T f16 operands") + ", PV " + ("f16" if args.v_layout == "tiles" else "bf16")
                             + " operands, fp32 accumulate")},

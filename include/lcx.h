@@ -153,7 +153,21 @@ typedef struct {
                                pre-rotated k has already been rounded); 2.1-2.2 times the
                                time of the default.  0: one product on operands rounded
                                once to f16. */
+  void* sched;              /* optional, LCX_SCHED_BYTES of device memory, 8-byte aligned,
+                               caller-owned, overwritten: the queue words of a dynamic work
+                               order (lcx_attn_fwd and each chunk of lcx_attn_fwd_chunked;
+                               ignored by lcx_attn_decode).  The hardware deals workgroups
+                               to the XCDs in turn, so in a static order each XCD does the
+                               same share of the work and a slower one keeps the others
+                               waiting at the end; with sched, workgroups take their work
+                               from per-XCD queues and XCDs that finish early take the last
+                               units of the others.  Results are identical either way.
+                               Calls that may run at the same time must not share it.
+                               NULL: static order. */
 } lcx_attn_args;
+
+/* Size of lcx_attn_args.sched. */
+#define LCX_SCHED_BYTES 64u
 
 /*
  * Steps a3 (fused) - a8: blockwise causal GQA attention with online softmax.
@@ -171,7 +185,8 @@ typedef struct {
  * rope_q or rope_k without rope, rope->head_dim != d, tables missing or not
  * covering the rotated positions, accumulate with a bf16 o, f16 with rope on,
  * precise_qk not 0/1; UNSUPPORTED for d not 64/128, causal == 0,
- * non-16-byte-aligned rows, precise_qk without rope_k.
+ * non-16-byte-aligned rows, precise_qk without rope_k, sched not 8-byte
+ * aligned.
  */
 lcx_status lcx_attn_fwd(const lcx_attn_args* a, hipStream_t stream);
 

@@ -46,7 +46,8 @@ class AttnArgs(ctypes.Structure):
                 ("cos_tab", _vp), ("sin_tab", _vp), ("tab_pos0", _i64), ("tab_len", _i64),
                 ("rope", ctypes.POINTER(RopeCfg)), ("softmax_scale", _f32), ("causal", _i32),
                 ("window", _i64), ("n_sink", _i32), ("o", _vp), ("o_dtype", _i32),
-                ("lse", _vp), ("accumulate", _i32), ("v_tiled", _i32), ("precise_qk", _i32)]
+                ("lse", _vp), ("accumulate", _i32), ("v_tiled", _i32), ("precise_qk", _i32),
+                ("sched", _vp)]
 
 
 class BwdArgs(ctypes.Structure):
@@ -199,8 +200,26 @@ def _workspace(t, name, shape):
                          f"got {t.dtype} {tuple(t.shape)} (contiguous: {t.is_contiguous()})")
 
 
+SCHED_BYTES = 64  # LCX_SCHED_BYTES
+
+
+def _sched(sched, device):
+    """The sched buffer of lcx_attn_args: True -> a new LCX_SCHED_BYTES device buffer
+    (dynamic work order), a tensor -> that buffer, False/None -> NULL (static order)."""
+    if sched is None or sched is False:
+        return None
+    if sched is True:
+        return torch.empty(SCHED_BYTES // 8, dtype=torch.int64, device=device)
+    if not isinstance(sched, torch.Tensor) or sched.device != device or \
+            sched.numel() * sched.element_size() < SCHED_BYTES or sched.data_ptr() % 8 or \
+            not sched.is_contiguous():
+        raise ValueError(f"sched must be a contiguous tensor of >= {SCHED_BYTES} bytes on {device}")
+    return sched
+
+
 def _attn_args(q, k, v, o, lse, *, rope_q, rope_k, cos, sin, tab_pos0, cfg, softmax_scale,
-               window, n_sink, q_pos0, k_pos0, accumulate, causal=True, precise_qk=False):
+               window, n_sink, q_pos0, k_pos0, accumulate, causal=True, precise_qk=False,
+               sched=None):
     _rows4(q, "q", dtypes=(torch.bfloat16, torch.float16))
     B, Hq, n_q, d = q.shape
     _rows4(k, "k", dtypes=(torch.bfloat16, torch.float16))
@@ -248,6 +267,7 @@ def _attn_args(q, k, v, o, lse, *, rope_q, rope_k, cos, sin, tab_pos0, cfg, soft
     a.lse = lse.data_ptr()
     a.accumulate = int(accumulate)
     a.precise_qk = int(precise_qk)
+    a.sched = sched.data_ptr() if sched is not None else None
     return a
 
 
@@ -267,10 +287,11 @@ def pack_v(v, out=None):
 
 def attn_fwd(q, k, v, o=None, lse=None, *, rope_q=False, rope_k=False, cos=None, sin=None,
              tab_pos0=0, rope=None, softmax_scale=0.0, window=-1, n_sink=0, q_pos0=0, k_pos0=0,
-             accumulate=False, out_dtype=torch.bfloat16, causal=True, precise_qk=False):
+             accumulate=False, out_dtype=torch.bfloat16, causal=True, precise_qk=False, sched=True):
     """lcx_attn_fwd.  q [B,Hq,n_q,d], k [B,Hkv,n_kv,d], v [B,Hkv,n_kv,d] or its pack_v
     tile layout.  precise_qk (with rope_k): QK^T from f16 high/low parts of the rotated
-    operands.  Returns (o, lse)."""
+    operands.  sched: True (a new queue buffer per call), a buffer of SCHED_BYTES, or
+    False for the static work order.  Returns (o, lse)."""
     B, Hq, n_q, d = q.shape
     if o is None:
         o = torch.empty((B, Hq, n_q, d), dtype=out_dtype, device=q.device)
@@ -279,7 +300,7 @@ def attn_fwd(q, k, v, o=None, lse=None, *, rope_q=False, rope_k=False, cos=None,
     a = _attn_args(q, k, v, o, lse, rope_q=rope_q, rope_k=rope_k, cos=cos, sin=sin,
                    tab_pos0=tab_pos0, cfg=rope, softmax_scale=softmax_scale, window=window,
                    n_sink=n_sink, q_pos0=q_pos0, k_pos0=k_pos0, accumulate=accumulate,
-                   causal=causal, precise_qk=precise_qk)
+                   causal=causal, precise_qk=precise_qk, sched=_sched(sched, q.device))
     _check(_lib.lcx_attn_fwd(ctypes.byref(a), _stream(q)))
     return o, lse
 
@@ -338,9 +359,10 @@ def attn_decode_noalloc(q, k, v, o, lse, *, n_splits=None, rope_q=False, cos=Non
 def attn_fwd_chunked(q, k, v, chunk: int, o_acc, lse_acc, o=None, lse=None, *, o_part=None,
                      lse_part=None, rope_q=False, rope_k=False, cos=None, sin=None, tab_pos0=0,
                      rope=None, softmax_scale=0.0, window=-1, n_sink=0, q_pos0=0, k_pos0=0,
-                     out_dtype=torch.bfloat16):
+                     out_dtype=torch.bfloat16, sched=True):
     """lcx_attn_fwd_chunked.  o_acc fp32 [B,Hq,n_q,d] / lse_acc fp32 [B,Hq,n_q] workspace;
-    o_part/lse_part (same shapes) select the separate merge pass.  Returns (o, lse)."""
+    o_part/lse_part (same shapes) select the separate merge pass; sched as in attn_fwd.
+    Returns (o, lse)."""
     B, Hq, n_q, d = q.shape
     _workspace(o_acc, "o_acc", (B, Hq, n_q, d))
     _workspace(lse_acc, "lse_acc", (B, Hq, n_q))
@@ -355,7 +377,8 @@ def attn_fwd_chunked(q, k, v, chunk: int, o_acc, lse_acc, o=None, lse=None, *, o
         lse = torch.empty((B, Hq, n_q), dtype=torch.float32, device=q.device)
     a = _attn_args(q, k, v, o, lse, rope_q=rope_q, rope_k=rope_k, cos=cos, sin=sin,
                    tab_pos0=tab_pos0, cfg=rope, softmax_scale=softmax_scale, window=window,
-                   n_sink=n_sink, q_pos0=q_pos0, k_pos0=k_pos0, accumulate=False)
+                   n_sink=n_sink, q_pos0=q_pos0, k_pos0=k_pos0, accumulate=False,
+                   sched=_sched(sched, q.device))
     _check(_lib.lcx_attn_fwd_chunked(ctypes.byref(a), chunk, _ptr(o_acc), _ptr(lse_acc),
                                      _ptr(o_part), _ptr(lse_part), _stream(q)))
     return o, lse

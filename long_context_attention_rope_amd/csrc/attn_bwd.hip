@@ -328,7 +328,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(const BwdParams
   const int l32 = lane & 31;
   const int h = lane >> 5;
 
-  const BlockTiles bt = block_tiles<32 * NW>(p);
+  const BlockTiles bt = block_tiles(p, (int)blockIdx.x, 32 * NW, 1);
   const int ntl = bt.ntl;
   const int64_t qi = bt.row0 + 32 * wave + l32;
   const bool qvalid = qi < p.n_q;

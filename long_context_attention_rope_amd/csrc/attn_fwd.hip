@@ -80,28 +80,52 @@ __device__ __forceinline__ int v_swz(int r) {
                   : ((4 * ((r >> 1) & 1)) ^ (2 * ((r >> 2) & 1)));
 }
 
+// The raw words of a lane's Q fragment (q[row][16c + 8h2 .. +7], c = 0 ..
+// D/16-1) and, for q_mode 2, their rows of the cos/sin tables.  Every load is
+// issued before any result is used, so the fragment costs one memory latency
+// rather than one per chunk; a row past the end reads row 0 and is zeroed at
+// use.
+template <int D>
+struct QRaw {
+  u32x4 raw[D / 16];
+  f32x4 cs[D / 16], sn[D / 16];
+  bool valid;
+  __device__ __forceinline__ void load(const AttnParams& p, const uint16_t* qbase, int64_t qi, int h2) {
+    valid = qi < p.n_q;
+    const int64_t r = valid ? qi : 0;
+    const uint16_t* q = qbase + r * p.qs_s + 8 * h2;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) raw[c] = *reinterpret_cast<const u32x4*>(q + 16 * c);
+    if (p.q_mode == 2) {
+      const int64_t t = (p.q_pos0 + r - p.tab_pos0) * (D / 2) + 4 * h2;
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        cs[c] = *reinterpret_cast<const f32x4*>(p.cos_tab + t + 8 * c);
+        sn[c] = *reinterpret_cast<const f32x4*>(p.sin_tab + t + 8 * c);
+      }
+    }
+  }
+  __device__ __forceinline__ u32x4 word(int c) const {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    return valid ? raw[c] : z;
+  }
+};
+
 // Q fragment for the B operand of S^T = K Q^T: lane (n, h2) holds
 // q[row n][16c + 8h2 .. +7] for c = 0 .. D/16-1, rotated, scaled by
 // sigma·log2(e) and rounded once to f16.
 template <int D>
 __device__ __forceinline__ void load_q(const AttnParams& p, const uint16_t* qbase, int64_t qi,
                                        int h2, f16x8 (&qf)[D / 16]) {
-  const bool valid = qi < p.n_q;
-  const int64_t trow = p.q_pos0 + qi - p.tab_pos0;
+  QRaw<D> q;
+  q.load(p, qbase, qi, h2);
   const float sc = p.scale_log2;
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
-    const int col = 16 * c + 8 * h2;
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (valid) raw = *reinterpret_cast<const u32x4*>(qbase + qi * p.qs_s + col);
+    const u32x4 raw = q.word(c);
     u32x4 w;
     if (p.q_mode == 2) {
-      f32x4 cs = {1.f, 1.f, 1.f, 1.f}, sn = {0.f, 0.f, 0.f, 0.f};
-      if (valid) {
-        cs = *reinterpret_cast<const f32x4*>(p.cos_tab + trow * (D / 2) + col / 2);
-        sn = *reinterpret_cast<const f32x4*>(p.sin_tab + trow * (D / 2) + col / 2);
-      }
-      w = rotate4_bf16<true>(raw, cs * sc, sn * sc);
+      w = rotate4_bf16<true>(raw, q.cs[c] * sc, q.sn[c] * sc);
     } else if (p.q_mode == 1) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) w[i] = pack_f16x2(bf16lo(raw[i]) * sc, bf16hi(raw[i]) * sc);
@@ -130,26 +154,19 @@ __device__ __forceinline__ F16Split split_f16x2(float a, float b) {
 template <int D>
 __device__ __forceinline__ void load_q_split(const AttnParams& p, const uint16_t* qbase, int64_t qi,
                                              int h2, f16x8 (&qh)[D / 16], f16x8 (&ql)[D / 16]) {
-  const bool valid = qi < p.n_q;
-  const int64_t trow = p.q_pos0 + qi - p.tab_pos0;
+  QRaw<D> q;
+  q.load(p, qbase, qi, h2);
   const float sc = p.scale_log2;
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
-    const int col = 16 * c + 8 * h2;
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (valid) raw = *reinterpret_cast<const u32x4*>(qbase + qi * p.qs_s + col);
+    const u32x4 raw = q.word(c);
     float x[8];
     if (p.q_mode == 2) {
-      f32x4 cs = {1.f, 1.f, 1.f, 1.f}, sn = {0.f, 0.f, 0.f, 0.f};
-      if (valid) {
-        cs = *reinterpret_cast<const f32x4*>(p.cos_tab + trow * (D / 2) + col / 2);
-        sn = *reinterpret_cast<const f32x4*>(p.sin_tab + trow * (D / 2) + col / 2);
-      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float x0 = bf16lo(raw[i]), x1 = bf16hi(raw[i]);
-        x[2 * i] = (x0 * cs[i] - x1 * sn[i]) * sc;
-        x[2 * i + 1] = (x0 * sn[i] + x1 * cs[i]) * sc;
+        x[2 * i] = (x0 * q.cs[c][i] - x1 * q.sn[c][i]) * sc;
+        x[2 * i + 1] = (x0 * q.sn[c][i] + x1 * q.cs[c][i]) * sc;
       }
     } else {
 #pragma unroll
@@ -692,6 +709,51 @@ __device__ __forceinline__ void operand_offsets(int lane, int (&koff)[D / 16], i
   }
 }
 
+// Dynamic work order of a forward launch.  The work units are the block ids
+// of the static order (block_tiles: longest causal rows first, unit v on XCD
+// v mod 8 next to the units that share its K/V in that XCD's L2).  The
+// hardware hands workgroups to the XCDs in turn (block id mod 8), so in the
+// static order every XCD gets the same share of the work, and an XCD that
+// runs slower than the others (they differ by a few per cent under this
+// load) leaves them idle at the end.  With p.sched the launch has more
+// workgroups than units; each takes a unit from the queue of its own XCD,
+// front first (longest first), and once that queue is empty takes the back
+// (shortest) unit of another queue, or exits when all are empty.  Faster
+// XCDs thus take over the last units of slower ones.  Queue x holds
+// v = x + 8i for i in [h, t): its 64-bit word packs h (low half) and t (high
+// half), set to (0, n_x) before the launch.  A front take adds 1 to h and
+// owns index h if h < t held; a back take lowers t by one with a
+// compare-and-swap only while h < t, so a failed take never moves t below h.
+// Returns the unit, or -1 when every queue is empty; called by one thread.
+__device__ __forceinline__ int take_unit(unsigned long long* q) {
+  const int x = blockIdx.x & 7;
+  {
+    const unsigned long long old = __hip_atomic_fetch_add(q + x, 1ull, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned h = (unsigned)old, t = (unsigned)(old >> 32);
+    if (h < t) return x + 8 * (int)h;
+  }
+  for (int k = 1; k < 8; ++k) {
+    unsigned long long* w = q + ((x + k) & 7);
+    unsigned long long old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (;;) {
+      const unsigned h = (unsigned)old, t = (unsigned)(old >> 32);
+      if (h >= t) break;
+      const unsigned long long nw = ((unsigned long long)(t - 1) << 32) | h;
+      if (__hip_atomic_compare_exchange_strong(w, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT))
+        return ((x + k) & 7) + 8 * (int)(t - 1);
+    }
+  }
+  return -1;
+}
+
+// the queue words before a launch with p.sched: (h, t) = (0, n_x)
+__global__ void sched_init_kernel(unsigned long long* q, int64_t n_units) {
+  const int x = threadIdx.x;
+  if (x < 8) q[x] = (unsigned long long)((n_units - x + 7) / 8) << 32;
+}
+
 template <int D, int KMODE, int NW, bool VT, bool PRECISE = false>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnParams p) {
   static_assert(!PRECISE || KMODE == 2, "the precise QK^T form splits the kernel's own rotation of k");
@@ -708,29 +770,42 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
   constexpr int EL = PRECISE ? T::ELEMS : 8;
   __shared__ __attribute__((aligned(1024))) uint16_t kl_st0[EL], kl_st1[EL];
 
+  __shared__ int next_unit;
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int h2 = lane >> 5;
 
-  const BlockTiles bt = block_tiles<T::BM>(p);
+  // the work unit: the block id, or (with p.sched) a unit taken from the
+  // queues
+  int unit = (int)blockIdx.x;
+  if (p.sched) {
+    if (tid == 0) next_unit = take_unit(p.sched);
+    __syncthreads();
+    unit = __builtin_amdgcn_readfirstlane(next_unit);
+    if (unit < 0) return;
+  }
+  // a workgroup holds p.hpb query heads of one KV head, NW / p.hpb waves of
+  // 32 rows each per head, so its waves cover the same positions and the
+  // tile range they share is the one each of them needs
+  const BlockTiles bt = block_tiles(p, unit, T::BM / p.hpb, p.hpb);
+  const int wph = NW / p.hpb;
+  const int hq = bt.hq + wave / wph;
+  const int64_t wrow0 = bt.row0 + 32 * (wave % wph);
   const int ntl = bt.ntl;
-  const uint16_t* qbase = p.q + bt.b * p.qs_b + bt.hq * p.qs_h;
+  const uint16_t* qbase = p.q + bt.b * p.qs_b + hq * p.qs_h;
   const uint16_t* kbase = p.k + bt.b * p.ks_b + bt.hkv * p.ks_h;
   const uint16_t* vbase = p.v + bt.b * p.vs_b + bt.hkv * p.vs_h;
 
   // the d = 128 kernels that stage K through registers or read V rows have
   // no 16 registers to spare
   Rows32<D, VT, D == 64 || (KMODE == 0 && VT)> rows;
-  rows.init(p, bt.row0 + wave * 32, l32);
-  // Q fragment (RoPE fused here when q_mode == 2); its low part in the
-  // precise form
+  rows.init(p, wrow0, l32);
+  // Q fragment (RoPE fused into its load when q_mode == 2) and its low part
+  // in the precise form; loaded below, once the first tiles are in flight
   f16x8 qf[D / 16], qlo[PRECISE ? D / 16 : 1];
-  if constexpr (PRECISE)
-    load_q_split<D>(p, qbase, rows.qi, h2, qf, qlo);
-  else
-    load_q<D>(p, qbase, rows.qi, h2, qf);
 
   // ---- staging and per-lane LDS read offsets
   LdsCopy<D, NW, true> kcp;
@@ -792,18 +867,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
   };
 
   if (ntl > 0) {
-    if constexpr (KMODE != 0) {
-      kreg.load(bt.j0(0));
+    if constexpr (KMODE != 0) kreg.load(bt.j0(0));
+    issue(k_st0, v_st0, 0);
+  }
+  if (NST > 2 && ntl > 1) issue(k_st1, v_st1, 1);
+  if constexpr (PRECISE)
+    load_q_split<D>(p, qbase, rows.qi, h2, qf, qlo);
+  else
+    load_q<D>(p, qbase, rows.qi, h2, qf);
+  if constexpr (KMODE != 0) {
+    if (ntl > 0) {
       if constexpr (PRECISE)
         kreg.store_split(k_st0, kl_st0);
       else
         kreg.store(k_st0);
     }
-    issue(k_st0, v_st0, 0);
   }
-  if (NST > 2 && ntl > 1) issue(k_st1, v_st1, 1);
-  // draining here costs one copy latency per workgroup and gives the loop a
-  // single entry state
+  // draining here costs one memory latency per workgroup and gives the loop
+  // a single entry state
   stage_barrier<0>();
   for (int t = 0; t < ntl; t += NST) {
     if constexpr (NST > 2) {
@@ -819,7 +900,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     }
   }
 
-  rows.store(p, bt.b, bt.hq, h2);
+  rows.store(p, bt.b, hq, h2);
 }
 
 // Decode: n_q <= 8 new query rows (positions q_pos0 ..) of all G query heads
@@ -987,30 +1068,51 @@ template __global__ void attn_decode_kernel<64, kDecNW, true, kDecNST64>(const A
 template __global__ void attn_decode_kernel<128, kDecNW, false, kDecNST128>(const AttnParams, const DecodeParams);
 template __global__ void attn_decode_kernel<128, kDecNW, true, kDecNST128>(const AttnParams, const DecodeParams);
 
-template <int D, int NW, bool VT>
-hipError_t launch_dv(const AttnParams& p, hipStream_t s, unsigned grid) {
-  const dim3 block(64 * NW);
-  switch (p.k_mode) {
-    case 0: hipLaunchKernelGGL((attn_fwd_kernel<D, 0, NW, VT>), dim3(grid), block, 0, s, p); break;
-    case 1: hipLaunchKernelGGL((attn_fwd_kernel<D, 1, NW, VT>), dim3(grid), block, 0, s, p); break;
-    default:
-      if (p.precise_qk)
-        hipLaunchKernelGGL((attn_fwd_kernel<D, 2, NW, VT, true>), dim3(grid), block, 0, s, p);
-      else
-        hipLaunchKernelGGL((attn_fwd_kernel<D, 2, NW, VT>), dim3(grid), block, 0, s, p);
-      break;
-  }
+template <class K>
+hipError_t launch_one(K kernel, const AttnParams& p, hipStream_t s, int64_t units, int block) {
+  if (p.sched) hipLaunchKernelGGL(sched_init_kernel, dim3(1), dim3(64), 0, s, p.sched, units);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)attn_fwd_grid(units, p.sched != nullptr)), dim3(block), 0, s, p);
   return hipGetLastError();
 }
 
+template <int D, int NW, bool VT>
+hipError_t launch_dv(const AttnParams& p, hipStream_t s, int64_t units) {
+  const int block = 64 * NW;
+  switch (p.k_mode) {
+    case 0: return launch_one(attn_fwd_kernel<D, 0, NW, VT>, p, s, units, block);
+    case 1: return launch_one(attn_fwd_kernel<D, 1, NW, VT>, p, s, units, block);
+    default:
+      if (p.precise_qk) return launch_one(attn_fwd_kernel<D, 2, NW, VT, true>, p, s, units, block);
+      return launch_one(attn_fwd_kernel<D, 2, NW, VT>, p, s, units, block);
+  }
+}
+
 template <int D, int NW>
-hipError_t launch_dn(const AttnParams& p, hipStream_t s, unsigned grid) {
-  return p.v_tiled ? launch_dv<D, NW, true>(p, s, grid) : launch_dv<D, NW, false>(p, s, grid);
+hipError_t launch_dn(const AttnParams& p, hipStream_t s, int64_t units) {
+  return p.v_tiled ? launch_dv<D, NW, true>(p, s, units) : launch_dv<D, NW, false>(p, s, units);
 }
 
 }  // namespace
 
-int attn_rows_per_block(int d) { return 32 * (d == 64 ? kNWd64 : kNWd128); }
+int attn_heads_per_block(int d, int G) {
+  const int nw = d == 64 ? kNWd64 : kNWd128;
+  int h = 1;
+  while (h < nw && G % (2 * h) == 0) h *= 2;
+  return h;
+}
+
+int64_t attn_fwd_blocks(int d, int B, int Hkv, int G, int64_t n_q) {
+  const int hpb = attn_heads_per_block(d, G);
+  const int span = 32 * (d == 64 ? kNWd64 : kNWd128) / hpb;
+  return (int64_t)B * Hkv * (G / hpb) * ((n_q + span - 1) / span);
+}
+
+int64_t attn_fwd_grid(int64_t units, bool dynamic) {
+  // with the dynamic order, an eighth more workgroups than units (a multiple
+  // of 8, so every XCD gets as many): an XCD can take up to that share of
+  // extra units from slower ones, and spare workgroups exit at once
+  return dynamic ? units + ((units + 63) / 64) * 8 : units;
+}
 
 hipError_t launch_attn_decode(const AttnParams& p, const DecodeParams& dp, hipStream_t s) {
   const dim3 grid((unsigned)dp.n_splits, (unsigned)p.Hkv, (unsigned)p.B), block(64 * kDecNW);
@@ -1030,14 +1132,15 @@ hipError_t launch_attn_decode(const AttnParams& p, const DecodeParams& dp, hipSt
 
 hipError_t launch_attn_fwd(const AttnParams& p_in, hipStream_t s) {
   AttnParams p = p_in;
-  const int bm = attn_rows_per_block(p.d);
-  p.n_qblk = (int32_t)((p.n_q + bm - 1) / bm);
+  p.hpb = attn_heads_per_block(p.d, p.G);
+  const int span = 32 * (p.d == 64 ? kNWd64 : kNWd128) / p.hpb;
+  p.n_qblk = (int32_t)((p.n_q + span - 1) / span);
   const int64_t units = (int64_t)p.B * p.Hkv * p.n_qblk;
   p.xcd_map = (units % 8 == 0) ? 1 : 0;
-  const int64_t grid = units * p.G;
-  if (grid == 0) return hipSuccess;
-  if (p.d == 64) return launch_dn<64, kNWd64>(p, s, (unsigned)grid);
-  return launch_dn<128, kNWd128>(p, s, (unsigned)grid);
+  const int64_t blocks = units * (p.G / p.hpb);
+  if (blocks == 0) return hipSuccess;
+  if (p.d == 64) return launch_dn<64, kNWd64>(p, s, blocks);
+  return launch_dn<128, kNWd128>(p, s, blocks);
 }
 
 }  // namespace lcx

@@ -104,10 +104,11 @@ __device__ __forceinline__ void lds_copy16_stream(__amdgpu_buffer_rsrc_t rsrc, u
 constexpr int kLoadStream = 3;  // sc0 | nt
 #pragma clang diagnostic pop
 
-// Block -> (batch, query head, 256-row query block) and the KV tiles it
-// visits: optional sink tiles, then the window / causal range.  Blocks run
-// longest causal rows first; with xcd_map the G query heads of one KV head
-// are consecutive on one XCD (block id mod 8), sharing its K/V in that L2.
+// Block (or work unit) bid -> (batch, KV head, hpb query heads of it starting
+// at hq, a query block of `span` rows) and the KV tiles it visits: optional
+// sink tiles, then the window / causal range.  Blocks run longest causal rows
+// first; with xcd_map the G / hpb blocks of one (KV head, query block) are
+// consecutive on one XCD (block id mod 8), sharing its K/V in that L2.
 struct BlockTiles {
   int b, hq, hkv;
   int64_t row0;
@@ -119,28 +120,28 @@ template <class P>
 __device__ __forceinline__ void tile_range(const P& p, int64_t qpos_min, int64_t qpos_max,
                                            BlockTiles& bt);
 
-template <int BM, class P>
-__device__ __forceinline__ BlockTiles block_tiles(const P& p) {
+template <class P>
+__device__ __forceinline__ BlockTiles block_tiles(const P& p, int bid, int span, int hpb) {
   BlockTiles bt;
-  const int bid = blockIdx.x;
+  const int gpb = p.G / hpb;  // blocks per (KV head, query block)
   int unit, g;
   if (p.xcd_map) {
     const int x = bid & 7;
     const int li = bid >> 3;
-    g = li % p.G;
-    unit = (li / p.G) * 8 + x;
+    g = li % gpb;
+    unit = (li / gpb) * 8 + x;
   } else {
-    unit = bid / p.G;
-    g = bid % p.G;
+    unit = bid / gpb;
+    g = bid % gpb;
   }
   bt.hkv = unit % p.Hkv;
   const int t1 = unit / p.Hkv;
   bt.b = t1 % p.B;
   const int qrank = t1 / p.B;
   const int qblk = p.n_qblk - 1 - qrank;
-  bt.hq = bt.hkv * p.G + g;
-  bt.row0 = (int64_t)qblk * BM;
-  const int64_t blk_last = (bt.row0 + BM < p.n_q ? bt.row0 + BM : p.n_q) - 1;
+  bt.hq = bt.hkv * p.G + g * hpb;
+  bt.row0 = (int64_t)qblk * span;
+  const int64_t blk_last = (bt.row0 + span < p.n_q ? bt.row0 + span : p.n_q) - 1;
   tile_range(p, p.q_pos0 + bt.row0, p.q_pos0 + blk_last, bt);
   return bt;
 }

@@ -172,6 +172,8 @@ lcx_status check_attn(const lcx_attn_args* a, bool chunked) {
   // pre-rotated k has already been rounded
   if (a->precise_qk && !a->rope_k)
     return fail(LCX_ERR_UNSUPPORTED, "precise_qk needs raw bf16 k rotated in the kernel (rope_k = 1)");
+  if ((reinterpret_cast<uintptr_t>(a->sched) & 7) != 0)
+    return fail(LCX_ERR_UNSUPPORTED, "sched must be 8-byte aligned");
   // tile layout: only the batch and head strides are used
   const int64_t v_st[3] = {a->v_strides[0], a->v_strides[1], a->v_tiled ? 8 : a->v_strides[2]};
   if (!strides_ok(a->q_strides, 8) || !strides_ok(a->k_strides, 8) || !strides_ok(v_st, 8))
@@ -185,9 +187,8 @@ lcx_status check_attn(const lcx_attn_args* a, bool chunked) {
   if (a->n_kv * a->k_strides[2] * 2 >= lim || (!a->v_tiled && a->n_kv * a->v_strides[2] * 2 >= lim) ||
       (a->rope_k && a->n_kv * a->d * 2 >= lim))
     return fail(LCX_ERR_UNSUPPORTED, "one KV head spans 2 GiB or more (split the keys into chunks)");
-  const int bm = lcx::attn_rows_per_block(a->d);
-  const int64_t nqblk = (a->n_q + bm - 1) / bm;
-  if ((int64_t)a->B * a->Hq * nqblk >= (int64_t)1 << 31)
+  if (lcx::attn_fwd_grid(lcx::attn_fwd_blocks(a->d, a->B, a->Hkv, a->Hq / a->Hkv, a->n_q),
+                         a->sched != nullptr) >= (int64_t)1 << 31)
     return fail(LCX_ERR_UNSUPPORTED, "problem too large for one launch");
   return LCX_OK;
 }
@@ -224,6 +225,7 @@ lcx::AttnParams make_params(const lcx_attn_args* a) {
   p.causal = a->causal;
   p.v_tiled = a->v_tiled;
   p.precise_qk = a->precise_qk;
+  p.sched = static_cast<unsigned long long*>(a->sched);
   return p;
 }
 
@@ -341,6 +343,7 @@ lcx_status check_decode(const lcx_attn_args* a, int32_t n_splits) {
 lcx_status run_decode(const lcx_attn_args* a, int32_t n_splits, float* o_part, float* lse_part,
                       hipStream_t stream) {
   lcx::AttnParams p = make_params(a);
+  p.sched = nullptr;  // decode has its own split of the work
   lcx::DecodeParams dp{o_part, lse_part, n_splits};
   hipError_t e = lcx::launch_attn_decode(p, dp, stream);
   if (e != hipSuccess) return hip_status(e, "decode launch");

@@ -55,9 +55,11 @@ struct AttnParams {
   int32_t k_mode;  // same codes, selects the kernel instantiation
   int32_t o_mode;  // 0: bf16, 1: f32, 2: f32 merged into the existing (o, lse)
   int32_t xcd_map; // 1: XCD-aware block order
+  int32_t hpb;     // query heads per workgroup (forward)
   int32_t causal;
   int32_t v_tiled;  // 1: v in the 64-key tile layout (vs_b, vs_h its strides)
   int32_t precise_qk;  // 1: QK^T from f16 high/low parts of q~ and k~ (k_mode 2 only)
+  unsigned long long* sched;  // 8 queue words: dynamic work order (NULL: one unit per block)
 };
 
 // backward pass (gradients of the attention rows)
@@ -155,6 +157,12 @@ hipError_t launch_finalize(const float* o_acc, const float* lse_acc, void* o, in
 constexpr int kBN = 64;      // keys per KV tile
 constexpr int kNWd64 = 4;    // waves (32 query rows each) per workgroup, d = 64
 constexpr int kNWd128 = 8;   // d = 128
-int attn_rows_per_block(int d);
+// query heads per forward workgroup (the largest power of two dividing G and
+// the wave count) and the forward grid size
+int attn_heads_per_block(int d, int G);
+int64_t attn_fwd_blocks(int d, int B, int Hkv, int G, int64_t n_q);
+// workgroups of a forward launch over `units` work units (dynamic: with the
+// queue words of AttnParams::sched)
+int64_t attn_fwd_grid(int64_t units, bool dynamic);
 
 }  // namespace lcx

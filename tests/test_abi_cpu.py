@@ -158,6 +158,8 @@ ATTN_BAD = [
     (1, dict(v_tiled=2)), (2, dict(v_tiled=1, v_strides=(ctypes.c_int64 * 3)(12, 16384, 0))),
     # precise QK^T: 0 or 1, and only on the kernel's own rotation of raw k
     (1, dict(precise_qk=2)), (2, dict(precise_qk=1)), (2, dict(precise_qk=1, k_dtype=2)),
+    # the dynamic work order's queue words are 64-bit
+    (2, dict(sched=FAKE + 4)),
 ]
 
 

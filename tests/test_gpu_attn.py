@@ -252,6 +252,67 @@ def test_deterministic_and_every_output_written(lcx):
     assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(l, l2)
 
 
+ORDER_CASES = [
+    # name, B, Hq, Hkv, d, n, window, n_sink, k_mode, v_tiled
+    ("g8_n2000", 1, 16, 2, 128, 2000, -1, 0, "pre_f16", True),   # 8 heads x 32 rows per workgroup
+    ("g4_win_sink", 1, 8, 2, 128, 1500, 300, 4, "pre_f16", True),  # 4 heads x 64 rows
+    ("g1_b2", 2, 3, 3, 128, 700, -1, 0, "pre_f16", False),  # 1 head x 256 rows
+    ("g3_d64_fused", 1, 6, 2, 64, 900, -1, 0, "fused", False),  # G = 3: 1 head x 128 rows
+    ("g16", 1, 16, 1, 128, 333, -1, 0, "pre_f16", True),  # 2 workgroups per query block
+    ("one_unit_precise", 1, 2, 1, 128, 40, -1, 0, "precise", False),  # 1 unit, 8 spare workgroups
+    ("d64_g2_win_b2", 2, 4, 2, 64, 1200, 100, 0, "pre_f16", True),
+]
+
+
+@pytest.mark.parametrize("name,B,Hq,Hkv,d,n,window,n_sink,k_mode,v_tiled", ORDER_CASES,
+                         ids=[c[0] for c in ORDER_CASES])
+def test_work_order_gives_identical_results(lcx, name, B, Hq, Hkv, d, n, window, n_sink, k_mode, v_tiled):
+    # every work unit computes the same rows whichever workgroup takes it, so
+    # the dynamic order (per-XCD queues, stealing, spare workgroups) must give
+    # the static order's outputs bit for bit and write every one of them
+    w = W.TINY.with_(B=B, Hq=Hq, Hkv=Hkv, d=d, n=n, window=window, n_sink=n_sink, seed=31,
+                     scheme="yarn", base=500000.0, L_train=256, L_target=1024, cur_len=1024)
+    q, k, v = U.inputs(w)
+    qd, kd, vd = U.to_dev(q), U.to_dev(k), U.to_dev(v)
+    if v_tiled:
+        vd = lcx.pack_v(vd)
+    cfg = _cfg(lcx, w)
+    cos, sin = lcx.rope_tables(cfg, n, device=U.dev())
+    fused = k_mode in ("fused", "precise")
+    kin = kd if fused else lcx.rope_apply_qk(None, kd, cos, sin)[1]
+    sched = torch.empty(lcx.SCHED_BYTES // 8, dtype=torch.int64, device=U.dev())
+    outs = []
+    for order in (False, sched, sched, True):  # static, the same buffer twice, a fresh one
+        o = torch.full((B, Hq, n, d), float("nan"), dtype=torch.bfloat16, device=U.dev())
+        l = torch.full((B, Hq, n), float("nan"), dtype=torch.float32, device=U.dev())
+        lcx.attn_fwd(qd, kin, vd, o, l, rope_q=True, rope_k=fused, cos=cos, sin=sin, rope=cfg,
+                     window=window, n_sink=n_sink, precise_qk=(k_mode == "precise"), sched=order)
+        torch.cuda.synchronize()
+        assert not torch.isnan(o).any() and not torch.isnan(l).any(), name
+        outs.append((o.view(torch.int16), l))
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1]), name
+
+
+def test_work_order_in_the_chunked_driver(lcx):
+    w = W.TINY.with_(n=1500, seed=12, Hq=8, Hkv=2, d=128, base=500000.0)
+    q, k, v = U.inputs(w)
+    qd, kd, vd = U.to_dev(q), U.to_dev(k), U.to_dev(v)
+    cfg = _cfg(lcx, w)
+    cos, sin = lcx.rope_tables(cfg, w.n, device=U.dev())
+    _, kr = lcx.rope_apply_qk(None, kd, cos, sin)
+    vt = lcx.pack_v(vd)
+    res = []
+    for order in (False, True):
+        acc_o = torch.empty((1, w.Hq, w.n, w.d), dtype=torch.float32, device=U.dev())
+        acc_l = torch.empty((1, w.Hq, w.n), dtype=torch.float32, device=U.dev())
+        o, l = lcx.attn_fwd_chunked(qd, kr, vt, 256, acc_o, acc_l, rope_q=True, cos=cos, sin=sin,
+                                    rope=cfg, sched=order)
+        torch.cuda.synchronize()
+        res.append((o.view(torch.int16), l))
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
 def test_rope_tables_match_oracle(lcx):
     pairs = W.LLAMA70B_128K.with_(name="70b_pair_factors", scheme="pair_factors",
                                   factors=_pair_factors(128, 7))
