@@ -454,10 +454,12 @@ def bench_backward(args, w):
     dv = torch.empty_like(dk)
     ws = torch.empty((w.B, w.Hq, w.n, 2), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    sched = torch.empty(lcx.SCHED_BYTES // 8, dtype=torch.int64, device=dev) \
+        if args.work_order == "dynamic" else False
 
     def step():
-        lcx.attn_bwd(qr, kr, v, o, lse, g, dq=dq, dk=dk, dv=dv, workspace=ws, unrotate=True, cos=cos,
-                     sin=sin, rope=cfg, window=w.window, n_sink=w.n_sink)
+        lcx.attn_bwd(qr, kr, v, o, lse, g, dq=dq, dk=dk, dv=dv, workspace=ws, sched=sched, unrotate=True,
+                     cos=cos, sin=sin, rope=cfg, window=w.window, n_sink=w.n_sink)
 
     for _ in range(args.warmup):
         step()
@@ -485,14 +487,15 @@ def bench_backward(args, w):
                    "head_dim": w.d, "seq_len": w.n, "rope": w.scheme, "causal": True,
                    "window": w.window, "n_sink": w.n_sink, "grads": "dq, dk, dv fp32 (raw q, k)",
                    "mfma": "bf16 operands (q~, k~, V, dO, P, dS), fp32 accumulate",
-                   "executed_products_per_pair": 7},
+                   "executed_products_per_pair": 7, "work_order": args.work_order},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "tokens_per_s": round(w.B * w.n / (ms_step * 1e-3), 1),
         "kernels_ms": {"attn_bwd (stats + dq + dk/dv)": round(bwd_ms, 3)},
         "roofline": {"kernel": "attn_bwd (stats + dq + dk/dv launches)", "bound": "mfma",
                      "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                     "traffic": bwd_traffic_from_profile() if w.name == "llama3_70b_128k_dynntk" else None},
+                     "traffic": bwd_traffic_from_profile()
+                     if w.name == "llama3_70b_128k_dynntk" and args.work_order == "dynamic" else None},
     }
     if args.cpu_rows > 0:
         out["cpu_baseline"] = cpu_baseline_bwd(w, args.cpu_rows)

@@ -334,6 +334,9 @@ typedef struct {
   int64_t dq_strides[3], dk_strides[3], dv_strides[3]; /* elements */
   float* workspace;         /* fp32 [B][Hq][n_q][2], contiguous, 16-byte aligned, caller-owned
                                scratch (per-row LSE·log2 e and D = <dO, O>) */
+  void* sched;              /* optional, LCX_SCHED_BYTES, 8-byte aligned, caller-owned,
+                               overwritten: the dynamic work order of the dq and dk/dv
+                               kernels, as lcx_attn_args.sched; NULL: static order */
 } lcx_attn_bwd_args;
 
 /*
@@ -355,7 +358,7 @@ typedef struct {
  * -1, n_sink < 0, bad dtypes, unrotate without rope or without tables covering
  * the positions, rope->head_dim != d;
  * UNSUPPORTED for d not 64/128, causal == 0, non-16-byte-aligned rows or
- * pointers, a row stride of 2^24 elements or more.
+ * pointers, a row stride of 2^24 elements or more, sched not 8-byte aligned.
  */
 lcx_status lcx_attn_bwd(const lcx_attn_bwd_args* a, hipStream_t stream);
 

@@ -61,7 +61,7 @@ class BwdArgs(ctypes.Structure):
                 ("unrotate", _i32), ("cos_tab", _vp), ("sin_tab", _vp), ("tab_pos0", _i64),
                 ("tab_len", _i64), ("dq", _vp), ("dk", _vp), ("dv", _vp), ("grad_dtype", _i32),
                 ("dq_strides", _i64 * 3), ("dk_strides", _i64 * 3), ("dv_strides", _i64 * 3),
-                ("workspace", _vp)]
+                ("workspace", _vp), ("sched", _vp)]
 
 
 _P3 = ctypes.POINTER(_i64)
@@ -405,12 +405,12 @@ def attn_merge(o_acc, lse_acc, o_part, lse_part, o_final=None):
 
 def attn_bwd(q, k, v, o, lse, dout, *, dq=None, dk=None, dv=None, workspace=None, unrotate=False,
              cos=None, sin=None, tab_pos0=0, rope=None, softmax_scale=0.0, window=-1, n_sink=0,
-             q_pos0=0, k_pos0=0, grad_dtype=torch.float32, causal=True):
+             q_pos0=0, k_pos0=0, grad_dtype=torch.float32, causal=True, sched=True):
     """lcx_attn_bwd.  q, k: the rotated bf16 q~ [B,Hq,n_q,d] and k~ [B,Hkv,n_kv,d] the
     forward used; v bf16 rows; o, lse: the forward's outputs; dout = dL/dO bf16.  With
     unrotate the gradients are those of the raw q, k (tables cos/sin required).
     Returns (dq, dk, dv) in grad_dtype; workspace (fp32 [B,Hq,n_q,2]) is allocated when
-    not given."""
+    not given; sched as in attn_fwd."""
     B, Hq, n_q, d = q.shape
     Hkv, n_kv = k.shape[1], k.shape[2]
     dev = q.device
@@ -459,5 +459,7 @@ def attn_bwd(q, k, v, o, lse, dout, *, dq=None, dk=None, dv=None, workspace=None
     a.grad_dtype = _DT[dq.dtype]
     a.dq_strides, a.dk_strides, a.dv_strides = _s3(dq), _s3(dk), _s3(dv)
     a.workspace = workspace.data_ptr()
+    sched = _sched(sched, dev)
+    a.sched = sched.data_ptr() if sched is not None else None
     _check(_lib.lcx_attn_bwd(ctypes.byref(a), _stream(q)))
     return dq, dk, dv

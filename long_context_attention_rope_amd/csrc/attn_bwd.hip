@@ -328,7 +328,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(const BwdParams
   const int l32 = lane & 31;
   const int h = lane >> 5;
 
-  const BlockTiles bt = block_tiles(p, (int)blockIdx.x, 32 * NW, 1);
+  __shared__ int unit_slot;
+  const int unit = workgroup_unit(p.sched, &unit_slot);
+  if (unit < 0) return;
+  const BlockTiles bt = block_tiles(p, unit, 32 * NW, 1);
   const int ntl = bt.ntl;
   const int64_t qi = bt.row0 + 32 * wave + l32;
   const bool qvalid = qi < p.n_q;
@@ -444,10 +447,10 @@ struct KeyBlock {
 };
 
 template <int KB>
-__device__ __forceinline__ KeyBlock key_block(const BwdParams& p) {
+__device__ __forceinline__ KeyBlock key_block(const BwdParams& p, int unit) {
   KeyBlock kb;
-  const int bh = (int)(blockIdx.x % (unsigned)(p.B * p.Hkv));
-  const int64_t blk = blockIdx.x / (unsigned)(p.B * p.Hkv);
+  const int bh = (int)((unsigned)unit % (unsigned)(p.B * p.Hkv));
+  const int64_t blk = (unsigned)unit / (unsigned)(p.B * p.Hkv);
   kb.hkv = bh % p.Hkv;
   kb.b = bh / p.Hkv;
   kb.key0 = blk * KB;
@@ -497,7 +500,10 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
   const int i16 = lane & 15;
   const int g = lane >> 4;
 
-  const KeyBlock kb = key_block<16 * NW>(p);
+  __shared__ int unit_slot;
+  const int unit = workgroup_unit(p.sched, &unit_slot);
+  if (unit < 0) return;
+  const KeyBlock kb = key_block<16 * NW>(p, unit);
   const int nrt = kb.t_hi - kb.t_lo;
   const int nsteps = nrt * p.G;
   const int64_t wkey0 = kb.key0 + 16 * wave;
@@ -728,15 +734,20 @@ hipError_t launch_bwd_d(const BwdParams& p_in, hipStream_t s) {
   p.n_qblk = (int32_t)((p.n_q + bm - 1) / bm);
   const int64_t units = (int64_t)p.B * p.Hkv * p.n_qblk;
   p.xcd_map = (units % 8 == 0) ? 1 : 0;
+  const bool dyn = p.sched != nullptr;
   if (units > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<D, NWQ>), dim3((unsigned)(units * p.G)), dim3(64 * NWQ), 0, s, p);
+    if (dyn) launch_sched_init(p.sched, units * p.G, s);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NWQ>), dim3((unsigned)sched_grid(units * p.G, dyn)), dim3(64 * NWQ),
+                       0, s, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   // dk, dv (every key; with no rows they are zeros)
   const int64_t kblk = (p.n_kv + 16 * kBwdNWk - 1) / (16 * kBwdNWk);
   if (kblk > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kBwdNWk>), dim3((unsigned)(kblk * p.B * p.Hkv)),
+    const int64_t kunits = kblk * p.B * p.Hkv;
+    if (dyn) launch_sched_init(p.sched, kunits, s);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kBwdNWk>), dim3((unsigned)sched_grid(kunits, dyn)),
                        dim3(64 * kBwdNWk), 0, s, p);
     return hipGetLastError();
   }

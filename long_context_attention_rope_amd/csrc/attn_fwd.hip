@@ -709,51 +709,6 @@ __device__ __forceinline__ void operand_offsets(int lane, int (&koff)[D / 16], i
   }
 }
 
-// Dynamic work order of a forward launch.  The work units are the block ids
-// of the static order (block_tiles: longest causal rows first, unit v on XCD
-// v mod 8 next to the units that share its K/V in that XCD's L2).  The
-// hardware hands workgroups to the XCDs in turn (block id mod 8), so in the
-// static order every XCD gets the same share of the work, and an XCD that
-// runs slower than the others (they differ by a few per cent under this
-// load) leaves them idle at the end.  With p.sched the launch has more
-// workgroups than units; each takes a unit from the queue of its own XCD,
-// front first (longest first), and once that queue is empty takes the back
-// (shortest) unit of another queue, or exits when all are empty.  Faster
-// XCDs thus take over the last units of slower ones.  Queue x holds
-// v = x + 8i for i in [h, t): its 64-bit word packs h (low half) and t (high
-// half), set to (0, n_x) before the launch.  A front take adds 1 to h and
-// owns index h if h < t held; a back take lowers t by one with a
-// compare-and-swap only while h < t, so a failed take never moves t below h.
-// Returns the unit, or -1 when every queue is empty; called by one thread.
-__device__ __forceinline__ int take_unit(unsigned long long* q) {
-  const int x = blockIdx.x & 7;
-  {
-    const unsigned long long old = __hip_atomic_fetch_add(q + x, 1ull, __ATOMIC_RELAXED,
-                                                          __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned h = (unsigned)old, t = (unsigned)(old >> 32);
-    if (h < t) return x + 8 * (int)h;
-  }
-  for (int k = 1; k < 8; ++k) {
-    unsigned long long* w = q + ((x + k) & 7);
-    unsigned long long old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (;;) {
-      const unsigned h = (unsigned)old, t = (unsigned)(old >> 32);
-      if (h >= t) break;
-      const unsigned long long nw = ((unsigned long long)(t - 1) << 32) | h;
-      if (__hip_atomic_compare_exchange_strong(w, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT))
-        return ((x + k) & 7) + 8 * (int)(t - 1);
-    }
-  }
-  return -1;
-}
-
-// the queue words before a launch with p.sched: (h, t) = (0, n_x)
-__global__ void sched_init_kernel(unsigned long long* q, int64_t n_units) {
-  const int x = threadIdx.x;
-  if (x < 8) q[x] = (unsigned long long)((n_units - x + 7) / 8) << 32;
-}
-
 template <int D, int KMODE, int NW, bool VT, bool PRECISE = false>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnParams p) {
   static_assert(!PRECISE || KMODE == 2, "the precise QK^T form splits the kernel's own rotation of k");
@@ -770,7 +725,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
   constexpr int EL = PRECISE ? T::ELEMS : 8;
   __shared__ __attribute__((aligned(1024))) uint16_t kl_st0[EL], kl_st1[EL];
 
-  __shared__ int next_unit;
+  __shared__ int unit_slot;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -778,15 +733,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
   const int l32 = lane & 31;
   const int h2 = lane >> 5;
 
-  // the work unit: the block id, or (with p.sched) a unit taken from the
-  // queues
-  int unit = (int)blockIdx.x;
-  if (p.sched) {
-    if (tid == 0) next_unit = take_unit(p.sched);
-    __syncthreads();
-    unit = __builtin_amdgcn_readfirstlane(next_unit);
-    if (unit < 0) return;
-  }
+  const int unit = workgroup_unit(p.sched, &unit_slot);
+  if (unit < 0) return;
   // a workgroup holds p.hpb query heads of one KV head, NW / p.hpb waves of
   // 32 rows each per head, so its waves cover the same positions and the
   // tile range they share is the one each of them needs
@@ -1070,8 +1018,8 @@ template __global__ void attn_decode_kernel<128, kDecNW, true, kDecNST128>(const
 
 template <class K>
 hipError_t launch_one(K kernel, const AttnParams& p, hipStream_t s, int64_t units, int block) {
-  if (p.sched) hipLaunchKernelGGL(sched_init_kernel, dim3(1), dim3(64), 0, s, p.sched, units);
-  hipLaunchKernelGGL(kernel, dim3((unsigned)attn_fwd_grid(units, p.sched != nullptr)), dim3(block), 0, s, p);
+  if (p.sched) launch_sched_init(p.sched, units, s);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)sched_grid(units, p.sched != nullptr)), dim3(block), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1107,11 +1055,21 @@ int64_t attn_fwd_blocks(int d, int B, int Hkv, int G, int64_t n_q) {
   return (int64_t)B * Hkv * (G / hpb) * ((n_q + span - 1) / span);
 }
 
-int64_t attn_fwd_grid(int64_t units, bool dynamic) {
+int64_t sched_grid(int64_t units, bool dynamic) {
   // with the dynamic order, an eighth more workgroups than units (a multiple
   // of 8, so every XCD gets as many): an XCD can take up to that share of
   // extra units from slower ones, and spare workgroups exit at once
   return dynamic ? units + ((units + 63) / 64) * 8 : units;
+}
+
+// the queue words before a launch with a sched buffer: (h, t) = (0, n_x)
+__global__ void sched_init_kernel(unsigned long long* q, int64_t n_units) {
+  const int x = threadIdx.x;
+  if (x < 8) q[x] = (unsigned long long)((n_units - x + 7) / 8) << 32;
+}
+
+void launch_sched_init(unsigned long long* sched, int64_t units, hipStream_t s) {
+  hipLaunchKernelGGL(sched_init_kernel, dim3(1), dim3(64), 0, s, sched, units);
 }
 
 hipError_t launch_attn_decode(const AttnParams& p, const DecodeParams& dp, hipStream_t s) {

@@ -176,6 +176,56 @@ __device__ __forceinline__ void tile_range(const P& p, int64_t qpos_min, int64_t
   bt.ntl = (int)(sink_t1 + (win_t1 - win_t0));
 }
 
+// Dynamic work order of a launch (forward and backward attention kernels).
+// The work units are the block ids of the kernel's static order (longest
+// rows first; unit v on XCD v mod 8 next to the units that share its K/V, or
+// its q~/dO, in that XCD's L2).  The hardware hands workgroups to the XCDs in
+// turn (block id mod 8), so in the static order every XCD gets the same
+// share of the work, and an XCD that runs slower than the others (they
+// differ by a few per cent under this load) leaves them idle at the end.
+// With a sched buffer the launch has more workgroups than units; each takes a
+// unit from the queue of its own XCD, front first (longest first), and once
+// that queue is empty takes the back (shortest) unit of another queue, or
+// exits when all are empty.  Faster XCDs thus take over the last units of
+// slower ones.  Queue x holds v = x + 8i for i in [h, t): its 64-bit word
+// packs h (low half) and t (high half), set to (0, n_x) before the launch
+// (launch_sched_init).  A front take adds 1 to h and owns index h if h < t
+// held; a back take lowers t by one with a compare-and-swap only while
+// h < t, so a failed take never moves t below h.  Returns the unit, or -1
+// when every queue is empty; called by one thread.
+__device__ __forceinline__ int take_unit(unsigned long long* q) {
+  const int x = blockIdx.x & 7;
+  {
+    const unsigned long long old = __hip_atomic_fetch_add(q + x, 1ull, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned h = (unsigned)old, t = (unsigned)(old >> 32);
+    if (h < t) return x + 8 * (int)h;
+  }
+  for (int k = 1; k < 8; ++k) {
+    unsigned long long* w = q + ((x + k) & 7);
+    unsigned long long old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (;;) {
+      const unsigned h = (unsigned)old, t = (unsigned)(old >> 32);
+      if (h >= t) break;
+      const unsigned long long nw = ((unsigned long long)(t - 1) << 32) | h;
+      if (__hip_atomic_compare_exchange_strong(w, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT))
+        return ((x + k) & 7) + 8 * (int)(t - 1);
+    }
+  }
+  return -1;
+}
+
+// The work unit of this workgroup: its block id, or with `sched` the unit
+// thread 0 takes from the queues, handed to every wave through `slot` (LDS);
+// -1 when the queues are empty.  Every thread of the workgroup calls it.
+__device__ __forceinline__ int workgroup_unit(unsigned long long* sched, int* slot) {
+  if (!sched) return (int)blockIdx.x;
+  if (threadIdx.x == 0) *slot = take_unit(sched);
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(*slot);
+}
+
 }  // namespace
 
 }  // namespace lcx

@@ -187,8 +187,8 @@ lcx_status check_attn(const lcx_attn_args* a, bool chunked) {
   if (a->n_kv * a->k_strides[2] * 2 >= lim || (!a->v_tiled && a->n_kv * a->v_strides[2] * 2 >= lim) ||
       (a->rope_k && a->n_kv * a->d * 2 >= lim))
     return fail(LCX_ERR_UNSUPPORTED, "one KV head spans 2 GiB or more (split the keys into chunks)");
-  if (lcx::attn_fwd_grid(lcx::attn_fwd_blocks(a->d, a->B, a->Hkv, a->Hq / a->Hkv, a->n_q),
-                         a->sched != nullptr) >= (int64_t)1 << 31)
+  if (lcx::sched_grid(lcx::attn_fwd_blocks(a->d, a->B, a->Hkv, a->Hq / a->Hkv, a->n_q),
+                      a->sched != nullptr) >= (int64_t)1 << 31)
     return fail(LCX_ERR_UNSUPPORTED, "problem too large for one launch");
   return LCX_OK;
 }
@@ -277,9 +277,12 @@ lcx_status check_bwd(const lcx_attn_bwd_args* a) {
   const int64_t lim = (int64_t)1 << 24;
   if (a->q_strides[2] >= lim || a->k_strides[2] >= lim || a->v_strides[2] >= lim || a->do_strides[2] >= lim)
     return fail(LCX_ERR_UNSUPPORTED, "row strides must be below 2^24 elements");
+  if ((reinterpret_cast<uintptr_t>(a->sched) & 7) != 0)
+    return fail(LCX_ERR_UNSUPPORTED, "sched must be 8-byte aligned");
   const int64_t bm = lcx::attn_bwd_rows_per_block(a->d), bk = lcx::attn_bwd_keys_per_block(a->d);
-  if ((int64_t)a->B * a->Hq * ((a->n_q + bm - 1) / bm) >= (int64_t)1 << 31 ||
-      (int64_t)a->B * a->Hkv * ((a->n_kv + bk - 1) / bk) >= (int64_t)1 << 31 ||
+  const bool dyn = a->sched != nullptr;
+  if (lcx::sched_grid((int64_t)a->B * a->Hq * ((a->n_q + bm - 1) / bm), dyn) >= (int64_t)1 << 31 ||
+      lcx::sched_grid((int64_t)a->B * a->Hkv * ((a->n_kv + bk - 1) / bk), dyn) >= (int64_t)1 << 31 ||
       (a->n_q + 63) / 64 * (a->Hq / a->Hkv) >= (int64_t)1 << 31)
     return fail(LCX_ERR_UNSUPPORTED, "problem too large for one launch");
   return LCX_OK;
@@ -294,6 +297,7 @@ lcx::BwdParams make_bwd_params(const lcx_attn_bwd_args* a) {
   p.lse = a->lse;
   p.dout = static_cast<const uint16_t*>(a->d_o);
   p.stats = a->workspace;
+  p.sched = static_cast<unsigned long long*>(a->sched);
   p.dq = a->dq; p.dk = a->dk; p.dv = a->dv;
   p.cos_tab = a->cos_tab; p.sin_tab = a->sin_tab;
   p.qs_b = a->q_strides[0]; p.qs_h = a->q_strides[1]; p.qs_s = a->q_strides[2];

@@ -97,6 +97,7 @@ struct BwdParams {
   int32_t o_f32;     // forward output in fp32 (else bf16)
   int32_t grad_f32;  // dq, dk, dv in fp32 (else bf16)
   int32_t unrotate;  // 1: dq, dk turned back by R(p)^T from the tables
+  unsigned long long* sched;  // 8 queue words: dynamic work order (NULL: one unit per block)
 };
 
 struct PackVParams {
@@ -161,8 +162,9 @@ constexpr int kNWd128 = 8;   // d = 128
 // the wave count) and the forward grid size
 int attn_heads_per_block(int d, int G);
 int64_t attn_fwd_blocks(int d, int B, int Hkv, int G, int64_t n_q);
-// workgroups of a forward launch over `units` work units (dynamic: with the
-// queue words of AttnParams::sched)
-int64_t attn_fwd_grid(int64_t units, bool dynamic);
+// workgroups of a launch over `units` work units (dynamic: with the queue
+// words of a sched buffer), and the kernel that sets those words first
+int64_t sched_grid(int64_t units, bool dynamic);
+void launch_sched_init(unsigned long long* sched, int64_t units, hipStream_t s);
 
 }  // namespace lcx

@@ -225,7 +225,7 @@ BWD_BAD = [
     (1, dict(unrotate=1, cos_tab=FAKE, sin_tab=FAKE, tab_len=256, k_pos0=1)),
     (1, dict(softmax_scale=float("nan"))), (2, dict(workspace=FAKE + 8)), (2, dict(dv=FAKE + 4)),
     (2, dict(do_strides=(ctypes.c_int64 * 3)(0, 0, 60))), (2, dict(dk_strides=(ctypes.c_int64 * 3)(0, 0, 66))),
-    (2, dict(k_strides=(ctypes.c_int64 * 3)(0, 0, 1 << 24))),
+    (2, dict(k_strides=(ctypes.c_int64 * 3)(0, 0, 1 << 24))), (2, dict(sched=FAKE + 4)),
 ]
 
 

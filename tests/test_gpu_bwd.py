@@ -191,6 +191,32 @@ def test_backward_empty_inputs(lcx):
     assert torch.all(dk == 0) and torch.all(dv == 0)
 
 
+@pytest.mark.parametrize("Hq,Hkv,d,n,window,n_sink,B", [(8, 2, 128, 700, -1, 0, 1), (4, 4, 64, 333, 100, 4, 2)])
+def test_backward_work_order_gives_identical_gradients(lcx, Hq, Hkv, d, n, window, n_sink, B):
+    # every dq row block and dk/dv key block is computed whole by the
+    # workgroup that takes it, so the dynamic order must reproduce the static
+    # order's gradients bit for bit (sched buffer reused, then a fresh one)
+    w = W.TINY.with_(B=B, Hq=Hq, Hkv=Hkv, d=d, n=n, window=window, n_sink=n_sink, seed=23,
+                     base=500000.0)
+    q, k, v = U.inputs(w)
+    qd, kd, vd, gd = U.to_dev(q), U.to_dev(k), U.to_dev(v), U.to_dev(_dout(w, n))
+    cfg = _cfg(lcx, w)
+    cos, sin = lcx.rope_tables(cfg, n, device=U.dev())
+    _, kf = lcx.rope_apply_qk(None, kd, cos, sin, out_dtype=torch.float16)
+    o, lse = lcx.attn_fwd(qd, kf, vd, rope_q=True, cos=cos, sin=sin, rope=cfg, window=window, n_sink=n_sink)
+    qr, kr = lcx.rope_apply_qk(qd, kd, cos, sin, out_dtype=torch.bfloat16)
+    sched = torch.empty(lcx.SCHED_BYTES // 8, dtype=torch.int64, device=U.dev())
+    res = []
+    for order in (False, sched, sched, True):
+        grads = lcx.attn_bwd(qr, kr, vd, o, lse, gd, unrotate=True, cos=cos, sin=sin, rope=cfg,
+                             window=window, n_sink=n_sink, sched=order)
+        torch.cuda.synchronize()
+        res.append(grads)
+    for grads in res[1:]:
+        for a, b in zip(res[0], grads):
+            assert torch.equal(a, b)
+
+
 def test_backward_deterministic(lcx):
     w = W.TINY.with_(Hq=8, Hkv=2, d=128, base=500000.0, n=1100, seed=15)
     q, k, v = U.inputs(w)
