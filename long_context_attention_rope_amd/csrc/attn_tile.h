@@ -107,8 +107,9 @@ constexpr int kLoadStream = 3;  // sc0 | nt
 // Block (or work unit) bid -> (batch, KV head, hpb query heads of it starting
 // at hq, a query block of `span` rows) and the KV tiles it visits: optional
 // sink tiles, then the window / causal range.  Blocks run longest causal rows
-// first; with xcd_map the G / hpb blocks of one (KV head, query block) are
-// consecutive on one XCD (block id mod 8), sharing its K/V in that L2.
+// first (first rows first under a short window); with xcd_map the G / hpb
+// blocks of one (KV head, query block) are consecutive on one XCD (block id
+// mod 8), sharing its K/V in that L2.
 struct BlockTiles {
   int b, hq, hkv;
   int64_t row0;
@@ -138,7 +139,13 @@ __device__ __forceinline__ BlockTiles block_tiles(const P& p, int bid, int span,
   const int t1 = unit / p.Hkv;
   bt.b = t1 % p.B;
   const int qrank = t1 / p.B;
-  const int qblk = p.n_qblk - 1 - qrank;
+  // longest causal rows first; under a window that covers at most a quarter
+  // of the rows, where nearly all blocks visit the same number of tiles, the
+  // first rows first instead: a block's first tiles (the start of its window)
+  // were then read by the blocks before it and hit in L2, where in the other
+  // order they are the ones no block has read yet
+  const bool first_rows_first = p.window >= 0 && (p.window + BN) * 4 <= p.n_q;
+  const int qblk = first_rows_first ? qrank : p.n_qblk - 1 - qrank;
   bt.hq = bt.hkv * p.G + g * hpb;
   bt.row0 = (int64_t)qblk * span;
   const int64_t blk_last = (bt.row0 + span < p.n_q ? bt.row0 + span : p.n_q) - 1;
