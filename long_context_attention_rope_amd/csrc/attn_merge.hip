@@ -188,6 +188,22 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const AttnParams p,
   const int64_t rows_all = (int64_t)p.B * p.Hq * nq;
   const int t = threadIdx.x;
   const int c = t % CG, sg = t / CG;
+  // The first PRE partials of this thread's splits (sg, sg + SG, ...) are
+  // loaded together with the LSEs the row maximum is taken over, so that one
+  // memory round trip serves both.  Every split writes its whole partial (an
+  // empty one O = 0 and LSE = -inf), so the loads need no condition; empty
+  // partials get weight 0.
+  constexpr int PRE = 4;
+  f32x4 o_pre[PRE];
+  float l_pre[PRE];
+#pragma unroll
+  for (int i = 0; i < PRE; ++i) {
+    const int sp = sg + i * SG;
+    const bool ok = sp < dp.n_splits;
+    const int64_t at = (ok ? sp : 0) * rows_all + row;
+    l_pre[i] = ok ? dp.lse_part[at] : -INFINITY;
+    o_pre[i] = load_once(reinterpret_cast<const f32x4*>(dp.o_part + at * D + 4 * c));
+  }
   // the largest partial LSE of the row (the reference for the weights)
   float m = -INFINITY;
   for (int sp = t; sp < dp.n_splits; sp += 256) m = fmaxf(m, dp.lse_part[sp * rows_all + row]);
@@ -196,17 +212,21 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const AttnParams p,
   if ((t & 63) == 0) wmax[t >> 6] = m;
   __syncthreads();
   const float mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  // weighted sums of this thread's splits: independent loads, no running rescale
+  // weighted sums of this thread's splits: no running rescale
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float l = 0.f;
-  for (int sp = sg; sp < dp.n_splits; sp += SG) {
-    const float ls = dp.lse_part[sp * rows_all + row];
-    if (ls == -INFINITY) continue;  // an empty partial (also every partial when mx is -inf)
-    const float w = expf(ls - mx);
-    const f32x4 o = load_once(reinterpret_cast<const f32x4*>(dp.o_part + (sp * rows_all + row) * D + 4 * c));
+  auto add = [&](float ls, const f32x4& o) {
+    // an empty partial (also every partial when mx is -inf) weighs 0
+    const float w = ls == -INFINITY ? 0.f : expf(ls - mx);
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] += w * o[e];
     l += w;
+  };
+#pragma unroll
+  for (int i = 0; i < PRE; ++i) add(l_pre[i], o_pre[i]);
+  for (int sp = sg + PRE * SG; sp < dp.n_splits; sp += SG) {
+    const int64_t at = sp * rows_all + row;
+    add(dp.lse_part[at], load_once(reinterpret_cast<const f32x4*>(dp.o_part + at * D + 4 * c)));
   }
   part[sg][c] = acc;
   if (c == 0) lsum[sg] = l;
