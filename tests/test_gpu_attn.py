@@ -261,6 +261,8 @@ ORDER_CASES = [
     ("g16", 1, 16, 1, 128, 333, -1, 0, "pre_f16", True),  # 2 workgroups per query block
     ("one_unit_precise", 1, 2, 1, 128, 40, -1, 0, "precise", False),  # 1 unit, 8 spare workgroups
     ("d64_g2_win_b2", 2, 4, 2, 64, 1200, 100, 0, "pre_f16", True),
+    # 4096 units, each running long enough that XCDs take units from each other
+    ("gqa8_16k_many_units", 1, 64, 8, 128, 16384, -1, 0, "pre_f16", True),
 ]
 
 

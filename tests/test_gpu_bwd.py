@@ -191,7 +191,8 @@ def test_backward_empty_inputs(lcx):
     assert torch.all(dk == 0) and torch.all(dv == 0)
 
 
-@pytest.mark.parametrize("Hq,Hkv,d,n,window,n_sink,B", [(8, 2, 128, 700, -1, 0, 1), (4, 4, 64, 333, 100, 4, 2)])
+@pytest.mark.parametrize("Hq,Hkv,d,n,window,n_sink,B", [(8, 2, 128, 700, -1, 0, 1), (4, 4, 64, 333, 100, 4, 2),
+                                                       (64, 8, 128, 8192, -1, 0, 1)])
 def test_backward_work_order_gives_identical_gradients(lcx, Hq, Hkv, d, n, window, n_sink, B):
     # every dq row block and dk/dv key block is computed whole by the
     # workgroup that takes it, so the dynamic order must reproduce the static
