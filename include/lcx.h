@@ -358,7 +358,8 @@ typedef struct {
  * -1, n_sink < 0, bad dtypes, unrotate without rope or without tables covering
  * the positions, rope->head_dim != d;
  * UNSUPPORTED for d not 64/128, causal == 0, non-16-byte-aligned rows or
- * pointers, a row stride of 2^24 elements or more, sched not 8-byte aligned.
+ * pointers, a row stride of 2^24 elements or more, sched not 8-byte aligned,
+ * n_q or n_kv above 2^31 - 64, more work units than one launch holds.
  */
 lcx_status lcx_attn_bwd(const lcx_attn_bwd_args* a, hipStream_t stream);
 

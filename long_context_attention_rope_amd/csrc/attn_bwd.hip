@@ -90,29 +90,27 @@ struct TileCopy {
   static constexpr int RPL = 1024 / (2 * D);
   static constexpr int LPW = BN / RPL / NW;
   static_assert(LPW >= 1 && BN == LPW * RPL * NW, "tile split");
-  int64_t rs;
-  int64_t n;
+  uint32_t rs2;  // row stride, bytes
   int row0;
   int lane;
 
-  __device__ __forceinline__ void init(int64_t stride, int64_t n_rows, int wave, int lane_) {
-    rs = stride;
-    n = n_rows;
+  __device__ __forceinline__ void init(int64_t stride, int wave, int lane_) {
+    rs2 = (uint32_t)(stride * 2);
     row0 = wave * LPW * RPL;
     lane = lane_;
   }
-  // the lane offsets are recomputed per copy (a few VALU ops) rather than
-  // held in registers across the step
-  __device__ __forceinline__ void issue(uint16_t* lds, const uint16_t* base, int64_t j0) const {
-    const int64_t left = n - j0;
-    const uint32_t rows = left <= 0 ? 0u : (left >= BN ? (uint32_t)BN : (uint32_t)left);
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + j0 * rs, rows * (uint32_t)(rs * 2));
+  // copy from the tile's first row (rows of them in range, the rest land as
+  // zeros) into the stage at LDS byte address lds_addr (wave-uniform); the
+  // lane offsets are recomputed per copy (a few VALU ops) rather than held
+  // in registers across the step
+  __device__ __forceinline__ void issue_rows(uint32_t lds_addr, const uint16_t* tile, uint32_t rows) const {
+    // rows is wave-uniform; readfirstlane keeps the resource in SGPRs
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(tile, __builtin_amdgcn_readfirstlane(rows * rs2));
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int row = row0 + i * RPL + lane / CPR;
-      const uint32_t off = (uint32_t)(row * rs * 2) + (uint32_t)(((lane % CPR) ^ tile_swz<D, S16>(row)) * 16);
-      const uint32_t la = (uint32_t)(uintptr_t)(lds_void*)(lds + (row0 + i * RPL) * D);
-      lds_copy16(r, off, __builtin_amdgcn_readfirstlane(la));
+      const uint32_t off = (uint32_t)row * rs2 + (uint32_t)(((lane % CPR) ^ tile_swz<D, S16>(row)) * 16);
+      lds_copy16(r, off, lds_addr + (uint32_t)((row0 + i * RPL) * D * 2));
     }
   }
 };
@@ -122,13 +120,9 @@ struct TileCopy {
 // float offset 2r.
 struct StatsCopy1 {
   static constexpr int FLOATS = 256;  // LDS floats per stage (64 lanes x 16 B)
-  __device__ static __forceinline__ void issue(float* lds, const float* rows_base, int64_t n_rows,
-                                               int64_t j0, int lane) {
-    const int64_t left = n_rows - j0;
-    const uint32_t rows = left <= 0 ? 0u : (left >= BN ? (uint32_t)BN : (uint32_t)left);
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(rows_base + 2 * j0, rows * 8u);
-    const uint32_t la = (uint32_t)(uintptr_t)(lds_void*)lds;
-    lds_copy16(r, (uint32_t)lane * 16u, __builtin_amdgcn_readfirstlane(la));
+  // from the statistics of the tile's first row (rows of them in range)
+  __device__ static __forceinline__ void issue_rows(uint32_t lds_addr, const float* first, uint32_t rows, int lane) {
+    lds_copy16(make_rsrc(first, __builtin_amdgcn_readfirstlane(rows * 8u)), (uint32_t)lane * 16u, lds_addr);
   }
 };
 
@@ -358,20 +352,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(const BwdParams
   C kcp, vcp;
   const uint16_t* kbase = p.k + bt.b * p.ks_b + bt.hkv * p.ks_h;
   const uint16_t* vbase = p.v + bt.b * p.vs_b + bt.hkv * p.vs_h;
-  kcp.init(p.ks_s, p.n_kv, wave, lane);
-  vcp.init(p.vs_s, p.n_kv, wave, lane);
+  kcp.init(p.ks_s, wave, lane);
+  vcp.init(p.vs_s, wave, lane);
   TileOffsets<D> to;
   to.init(lane);
 
   constexpr int kLoads = 2 * C::LPW;
-  auto issue = [&](uint16_t* ks, uint16_t* vs, int t) {
+  const uint32_t lk = (uint32_t)(uintptr_t)(lds_void*)&k_st[0][0];
+  const uint32_t lv = (uint32_t)(uintptr_t)(lds_void*)&v_st[0][0];
+  auto issue = [&](int st, int t) {
     const int j0 = bt.j0(t);
-    kcp.issue(ks, kbase, j0);
-    vcp.issue(vs, vbase, j0);
+    const int left = (int)p.n_kv - j0;  // n_kv < 2^31
+    const uint32_t rows = left <= 0 ? 0u : (left >= BN ? (uint32_t)BN : (uint32_t)left);
+    kcp.issue_rows(lk + (uint32_t)(st * TE * 2), kbase + (int64_t)j0 * p.ks_s, rows);
+    vcp.issue_rows(lv + (uint32_t)(st * TE * 2), vbase + (int64_t)j0 * p.vs_s, rows);
   };
-  auto step = [&](const uint16_t* ks, const uint16_t* vs, uint16_t* ks_next, uint16_t* vs_next, int t) {
+  auto step = [&](const uint16_t* ks, const uint16_t* vs, int nxt, int t) {
     const bool pre = t + 2 < ntl;
-    if (pre) issue(ks_next, vs_next, t + 2);
+    if (pre) issue(nxt, t + 2);
     const int j0 = bt.j0(t);
     // two halves of 32 keys: S^T, dP^T, then dQ^T over those keys
 #pragma unroll
@@ -408,13 +406,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(const BwdParams
       stage_barrier<0>();
   };
 
-  if (ntl > 0) issue(k_st[0], v_st[0], 0);
-  if (ntl > 1) issue(k_st[1], v_st[1], 1);
+  if (ntl > 0) issue(0, 0);
+  if (ntl > 1) issue(1, 1);
   stage_barrier<0>();
   // tile t is in stage t % 3; tile t + 2 goes to stage (t + 2) % 3
   int cur = 0, nxt = 2;
   for (int t = 0; t < ntl; ++t) {
-    step(k_st[cur], v_st[cur], k_st[nxt], v_st[nxt], t);
+    step(k_st[cur], v_st[cur], nxt, t);
     cur = cur == 2 ? 0 : cur + 1;
     nxt = nxt == 2 ? 0 : nxt + 1;
   }
@@ -567,35 +565,61 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
   }
 
   C qcp, gcp;
-  qcp.init(p.qs_s, p.n_q, wave, lane);
-  gcp.init(p.dos_s, p.n_q, wave, lane);
-  auto step_rows = [&](int s) -> int64_t { return (int64_t)(kb.t_hi - 1 - s / p.G) * BN; };
-  auto step_head = [&](int s) -> int { return kb.hkv * p.G + s % p.G; };
-  auto issue = [&](uint16_t* qs, uint16_t* gs, float* ss, int s) {
-    const int64_t j0 = step_rows(s);
-    const int hq = step_head(s);
-    qcp.issue(qs, p.q + kb.b * p.qs_b + hq * p.qs_h, j0);
-    gcp.issue(gs, p.dout + kb.b * p.dos_b + hq * p.dos_h, j0);
+  qcp.init(p.qs_s, wave, lane);
+  gcp.init(p.dos_s, wave, lane);
+  // Copy sources of the next step to issue (row tile it, head hkv·G + ig),
+  // advanced per issue: steps run over the G heads of a row tile, then the
+  // row tile above (no divisions, pointers moved by their strides)
+  int it = kb.t_hi - 1, ig = 0;
+  const int64_t hq0 = (int64_t)kb.hkv * p.G;
+  const uint16_t* iq = p.q + kb.b * p.qs_b + hq0 * p.qs_h + (int64_t)it * BN * p.qs_s;
+  const uint16_t* igo = p.dout + kb.b * p.dos_b + hq0 * p.dos_h + (int64_t)it * BN * p.dos_s;
+  const float* ist = p.stats + 2 * (((int64_t)kb.b * p.Hq + hq0) * p.n_q + (int64_t)it * BN);
+  const int64_t q_wrap = (int64_t)(p.G - 1) * p.qs_h + (int64_t)BN * p.qs_s;
+  const int64_t g_wrap = (int64_t)(p.G - 1) * p.dos_h + (int64_t)BN * p.dos_s;
+  const int64_t s_wrap = 2 * ((int64_t)(p.G - 1) * p.n_q + BN);
+  const uint32_t lq = (uint32_t)(uintptr_t)(lds_void*)&q_st[0][0];
+  const uint32_t lg = (uint32_t)(uintptr_t)(lds_void*)&g_st[0][0];
+  const uint32_t ls = (uint32_t)(uintptr_t)(lds_void*)&s_st[0][0];
+  auto issue_next = [&](int st) {
+    const int left = (int)p.n_q - it * BN;  // n_q < 2^31
+    const uint32_t rows = left <= 0 ? 0u : (left >= BN ? (uint32_t)BN : (uint32_t)left);
+    qcp.issue_rows(lq + (uint32_t)(st * TE * 2), iq, rows);
+    gcp.issue_rows(lg + (uint32_t)(st * TE * 2), igo, rows);
     // the statistics come with wave 0's copies (one 512-byte load instead
     // of one small load per wave)
-    if (wave == 0) StatsCopy1::issue(ss, p.stats + 2 * ((int64_t)kb.b * p.Hq + hq) * p.n_q, p.n_q, j0, lane);
+    if (wave == 0) StatsCopy1::issue_rows(ls + (uint32_t)(st * SE * 4), ist, rows, lane);
+    if (++ig == p.G) {
+      ig = 0;
+      --it;
+      iq -= q_wrap;
+      igo -= g_wrap;
+      ist -= s_wrap;
+    } else {
+      iq += p.qs_h;
+      igo += p.dos_h;
+      ist += 2 * p.n_q;
+    }
   };
   constexpr int kLoads = 2 * C::LPW;  // vector memory ops per step (wave 0: one more)
 
-  auto step = [&](const uint16_t* qs, const uint16_t* gs, const float* ss, uint16_t* qs_n, uint16_t* gs_n,
-                  float* ss_n, int s) {
+  int ct = kb.t_hi - 1, cg = 0;  // row tile and head of the step
+  auto step = [&](const uint16_t* qs, const uint16_t* gs, const float* ss, int nxt, int s) {
     const bool pre = s + 2 < nsteps;
-    if (pre) issue(qs_n, gs_n, ss_n, s + 2);
-    const int64_t j0 = step_rows(s);
-    const int64_t qpos_t = p.q_pos0 + j0;
-    const bool all_kept = keys_whole && (int)j0 >= rt_lo && (int)j0 <= rt_hi;
-    const int hi = clamp_i32(qpos_t - kpos);  // causal: row off kept iff hi + off >= 0
-    const int lo = p.window >= 0 ? clamp_i32(qpos_t - kpos - p.window) : -(1 << 30);  // lo + off <= 0
-    const int rrem = clamp_tile(p.n_q - j0);
-    // S and dP of both 32-row halves first, then the masks (one branch), then
-    // per half the softmax and the dV/dK products: the second half's products
-    // are in flight while the first half's softmax runs, and the softmax of
-    // the second half can overlap the first half's dV/dK products
+    if (pre) issue_next(nxt);
+    const int j0 = ct * BN;
+    if (++cg == p.G) {
+      cg = 0;
+      --ct;
+    }
+    const bool all_kept = keys_whole && j0 >= rt_lo && j0 <= rt_hi;
+    // The step in four runs of 16 products, each operand read issued four
+    // products ahead and the order fixed by scheduling barriers: S and dP of
+    // rows 0-31 (half 0); S and dP of half 1 with the softmax of half 0
+    // between the products; the masks (one branch); dV^T and dK^T of half 0
+    // with the softmax of half 1 between them; dV^T and dK^T of half 1.  The
+    // exponentials and the products of the other half then share the SIMD
+    // instead of taking turns.
     f32x4 sc[2][2], dp[2][2];  // [half kc][row block u]
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
@@ -606,23 +630,70 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
           sc[kc][u][r] = 0.f;
           dp[kc][u][r] = 0.f;
         }
+    // statistics of the lane's rows 32kc + 16u + 4g + {0..3}: LSE·log2 e, D
+    float l2[2][2][4], dd[2][2][4];
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c)
+      for (int u = 0; u < 2; ++u) {
+        const int row = 32 * kc + 16 * u + 4 * g;
+        const f32x4 ta = *reinterpret_cast<const f32x4*>(ss + 2 * row);
+        const f32x4 tc = *reinterpret_cast<const f32x4*>(ss + 2 * row + 4);
+        l2[kc][u][0] = ta[0];
+        dd[kc][u][0] = ta[1];
+        l2[kc][u][1] = ta[2];
+        dd[kc][u][1] = ta[3];
+        l2[kc][u][2] = tc[0];
+        dd[kc][u][2] = tc[1];
+        l2[kc][u][3] = tc[2];
+        dd[kc][u][3] = tc[3];
+      }
+    // P = exp2(S·sigma·log2 e - LSE·log2 e) and dS = P (dP - D) of value v
+    // (row block v / 4, register v % 4) of half kc, in place
+    auto soft = [&](int kc, int v) {
+      const int u = v >> 2, r = v & 3;
+      const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kc][u][r], p.scale_log2, -l2[kc][u][r]));
+      sc[kc][u][r] = pr;
+      dp[kc][u][r] = pr * (dp[kc][u][r] - dd[kc][u][r]);
+    };
+    // S / dP products: i -> chunk c = i / 4, row block u = (i / 2) % 2, S or dP
+    constexpr int NS = 4 * (D / 32);
+    auto rd_s = [&](int kc, int i) {
+      const int c = i >> 2, u = (i >> 1) & 1, rb = 2 * kc + u;
+      return *reinterpret_cast<const bf16x8*>((i & 1 ? gs : qs) + rb * 16 * D + roff[c]);
+    };
+    auto mfma_s = [&](int kc, int i, const bf16x8& a) {
+      const int c = i >> 2, u = (i >> 1) & 1;
+      if (i & 1)
+        dp[kc][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, vf[c], dp[kc][u], 0, 0, 0);
+      else
+        sc[kc][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kf[c], sc[kc][u], 0, 0, 0);
+    };
+    {
+      constexpr int AH = 4;
+      bf16x8 a[2 * NS];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int rb = 2 * kc + u;
-          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qs + rb * 16 * D + roff[c]);
-          const bf16x8 ag = *reinterpret_cast<const bf16x8*>(gs + rb * 16 * D + roff[c]);
-          sc[kc][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, kf[c], sc[kc][u], 0, 0, 0);
-          dp[kc][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, vf[c], dp[kc][u], 0, 0, 0);
+      for (int i = 0; i < AH; ++i) a[i] = rd_s(0, i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 2 * NS; ++i) {
+        mfma_s(i / NS, i % NS, a[i]);
+        if (i + AH < 2 * NS) a[i + AH] = rd_s((i + AH) / NS, (i + AH) % NS);
+        if (i >= NS) {
+#pragma unroll
+          for (int v = (i - NS) * 8 / NS; v < (i - NS + 1) * 8 / NS; ++v) soft(0, v);
         }
-    // each product's operand read issued four products ahead (left to itself
-    // the scheduler kept one or two in flight: 932 -> 917 ms per backward)
-    pipeline_reads<4 * D / 16, 1, 4, 7>();
-    // element (kc, u, r) is row 32kc + 16u + 4g + r of the tile and the lane's key
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // element (kc, u, r) is row 32kc + 16u + 4g + r of the tile and the lane's
+    // key; half 0 holds P and dS already (its pairs outside the mask become
+    // 0, whatever their exponential gave), half 1 still S
     if (!all_kept) {
+      const int64_t qpos_t = p.q_pos0 + j0;
+      const int hi = clamp_i32(qpos_t - kpos);  // causal: row off kept iff hi + off >= 0
+      const int lo = p.window >= 0 ? clamp_i32(qpos_t - kpos - p.window) : -(1 << 30);  // lo + off <= 0
+      const int rrem = clamp_tile(p.n_q - (int64_t)j0);
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
@@ -631,45 +702,58 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
           for (int r = 0; r < 4; ++r) {
             const int off = 32 * kc + 16 * u + 4 * g + r;
             const bool ok = kvalid & (off < rrem) & (!p.causal | (hi + off >= 0)) & ((lo + off <= 0) | k_sink);
-            sc[kc][u][r] = ok ? sc[kc][u][r] : -INFINITY;
+            if (kc == 0) {
+              sc[0][u][r] = ok ? sc[0][u][r] : 0.f;
+              dp[0][u][r] = ok ? dp[0][u][r] : 0.f;
+            } else {
+              sc[1][u][r] = ok ? sc[1][u][r] : -INFINITY;
+            }
           }
     }
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      // P = exp2(S·sigma·log2 e - LSE·log2 e), dS = P (dP - D)
+    auto pack = [&](int kc, bf16x8& pf, bf16x8& dsf) {
       u32x4 wp, wd;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int row = 32 * kc + 16 * u + 4 * g;
-        const f32x4 ta = *reinterpret_cast<const f32x4*>(ss + 2 * row);
-        const f32x4 tc = *reinterpret_cast<const f32x4*>(ss + 2 * row + 4);
-        const float l2[4] = {ta[0], ta[2], tc[0], tc[2]};
-        const float dd[4] = {ta[1], ta[3], tc[1], tc[3]};
-        float pr[4], ds[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kc][u][r], p.scale_log2, -l2[r]));
-          ds[r] = pr[r] * (dp[kc][u][r] - dd[r]);
-        }
-        wp[2 * u] = pack_bf16x2(pr[0], pr[1]);
-        wp[2 * u + 1] = pack_bf16x2(pr[2], pr[3]);
-        wd[2 * u] = pack_bf16x2(ds[0], ds[1]);
-        wd[2 * u + 1] = pack_bf16x2(ds[2], ds[3]);
+        wp[2 * u] = pack_bf16x2(sc[kc][u][0], sc[kc][u][1]);
+        wp[2 * u + 1] = pack_bf16x2(sc[kc][u][2], sc[kc][u][3]);
+        wd[2 * u] = pack_bf16x2(dp[kc][u][0], dp[kc][u][1]);
+        wd[2 * u + 1] = pack_bf16x2(dp[kc][u][2], dp[kc][u][3]);
       }
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, wp);
-      const bf16x8 dsf = __builtin_bit_cast(bf16x8, wd);
-      // dV^T += dO^T·P, dK^T += Q^T·dS over the half's 32 rows
+      pf = __builtin_bit_cast(bf16x8, wp);
+      dsf = __builtin_bit_cast(bf16x8, wd);
+    };
+    // dV^T += dO^T·P, dK^T += Q^T·dS over a half's 32 rows: i -> d-block
+    // db = i / 2, dV or dK
+    auto rd_t = [&](int kc, int i) {
+      const int o0 = toff[i >> 1] + kc * 32 * D;
+      const uint16_t* t = i & 1 ? qs : gs;
+      const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(t + o0));
+      const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(t + o0 + 16 * D));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    constexpr int NT = 2 * (D / 16);
+    bf16x8 pf[2], dsf[2];
+    pack(0, pf[0], dsf[0]);
+    {
+      constexpr int AH = 4;
+      bf16x8 a[2 * NT];
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        const int o0 = toff[db] + kc * 32 * D;
-        const v4i16 g0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(gs + o0));
-        const v4i16 g1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(gs + o0 + 16 * D));
-        const v4i16 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(qs + o0));
-        const v4i16 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(qs + o0 + 16 * D));
-        const bf16x8 ga = __builtin_bit_cast(bf16x8, __builtin_shufflevector(g0, g1, 0, 1, 2, 3, 4, 5, 6, 7));
-        const bf16x8 qa = __builtin_bit_cast(bf16x8, __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7));
-        dvacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga, pf, dvacc[db], 0, 0, 0);
-        dkacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, dsf, dkacc[db], 0, 0, 0);
+      for (int i = 0; i < AH; ++i) a[i] = rd_t(0, i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 2 * NT; ++i) {
+        const int kc = i / NT, j = i % NT;
+        if (i == NT) pack(1, pf[1], dsf[1]);
+        if (j & 1)
+          dkacc[j >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], dsf[kc], dkacc[j >> 1], 0, 0, 0);
+        else
+          dvacc[j >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], pf[kc], dvacc[j >> 1], 0, 0, 0);
+        if (i + AH < 2 * NT) a[i + AH] = rd_t((i + AH) / NT, (i + AH) % NT);
+        if (i < NT) {
+#pragma unroll
+          for (int v = i * 8 / NT; v < (i + 1) * 8 / NT; ++v) soft(1, v);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (!pre)
@@ -680,12 +764,12 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
       stage_barrier<kLoads>();
   };
 
-  if (nsteps > 0) issue(q_st[0], g_st[0], s_st[0], 0);
-  if (nsteps > 1) issue(q_st[1], g_st[1], s_st[1], 1);
+  if (nsteps > 0) issue_next(0);
+  if (nsteps > 1) issue_next(1);
   stage_barrier<0>();
   int cur = 0, nxt = 2;
   for (int s = 0; s < nsteps; ++s) {
-    step(q_st[cur], g_st[cur], s_st[cur], q_st[nxt], g_st[nxt], s_st[nxt], s);
+    step(q_st[cur], g_st[cur], s_st[cur], nxt, s);
     cur = cur == 2 ? 0 : cur + 1;
     nxt = nxt == 2 ? 0 : nxt + 1;
   }

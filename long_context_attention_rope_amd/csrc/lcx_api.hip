@@ -281,6 +281,9 @@ lcx_status check_bwd(const lcx_attn_bwd_args* a) {
     return fail(LCX_ERR_UNSUPPORTED, "sched must be 8-byte aligned");
   const int64_t bm = lcx::attn_bwd_rows_per_block(a->d), bk = lcx::attn_bwd_keys_per_block(a->d);
   const bool dyn = a->sched != nullptr;
+  // row and key indices of a tile are 32-bit in the kernels
+  if (a->n_q > ((int64_t)1 << 31) - 64 || a->n_kv > ((int64_t)1 << 31) - 64)
+    return fail(LCX_ERR_UNSUPPORTED, "n_q and n_kv must be below 2^31 - 64");
   if (lcx::sched_grid((int64_t)a->B * a->Hq * ((a->n_q + bm - 1) / bm), dyn) >= (int64_t)1 << 31 ||
       lcx::sched_grid((int64_t)a->B * a->Hkv * ((a->n_kv + bk - 1) / bk), dyn) >= (int64_t)1 << 31 ||
       (a->n_q + 63) / 64 * (a->Hq / a->Hkv) >= (int64_t)1 << 31)

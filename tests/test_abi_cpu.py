@@ -226,6 +226,7 @@ BWD_BAD = [
     (1, dict(softmax_scale=float("nan"))), (2, dict(workspace=FAKE + 8)), (2, dict(dv=FAKE + 4)),
     (2, dict(do_strides=(ctypes.c_int64 * 3)(0, 0, 60))), (2, dict(dk_strides=(ctypes.c_int64 * 3)(0, 0, 66))),
     (2, dict(k_strides=(ctypes.c_int64 * 3)(0, 0, 1 << 24))), (2, dict(sched=FAKE + 4)),
+    (2, dict(n_q=(1 << 31) - 63)), (2, dict(n_kv=(1 << 31) - 63)),
 ]
 
 
