@@ -282,7 +282,7 @@ struct KeptTiles {
     lo = p.window >= 0 ? sat(qpos_max - p.window - p.k_pos0) : INT32_MIN;
     sink = sat((int64_t)p.n_sink - p.k_pos0 - (BN - 1));
   }
-  __device__ __forceinline__ bool whole(int j0) const { return j0 <= hi && (j0 >= lo || j0 < sink); }
+  __device__ __forceinline__ bool whole(int j0) const { return (j0 <= hi) & ((j0 >= lo) | (j0 < sink)); }
 };
 
 // Key mask of half kb of a 64-key tile for the lane's query row (S^T
@@ -290,9 +290,8 @@ struct KeptTiles {
 // that every row of the wave keeps whole are left alone.  The lane's key
 // offset is bias + c with c a constant of the unrolled loop: the bounds are
 // shifted by bias once and each element compares against an inline constant.
-__device__ __forceinline__ void mask_keys(const BwdParams& p, f32x16& s, int j0, int kb, int64_t qpos,
-                                          const KeptTiles& kt, int h) {
-  if (kt.whole(j0)) return;
+__device__ __forceinline__ void mask_keys(const BwdParams& p, f32x16& s, int j0, int kb, int64_t qpos, int h,
+                                          float fill) {
   const int64_t kpos_min = p.k_pos0 + j0;
   const int64_t rel = qpos - kpos_min;
   const int hi = p.causal ? clamp_i32(rel) : (1 << 30);
@@ -305,7 +304,7 @@ __device__ __forceinline__ void mask_keys(const BwdParams& p, f32x16& s, int j0,
   for (int r = 0; r < 16; ++r) {
     const int c = (r >> 2) * 8 + (r & 3);
     const bool ok = (c < a_k) & (c <= a_hi) & ((c >= a_lo) | (c < a_s));
-    s[r] = ok ? s[r] : -INFINITY;
+    s[r] = ok ? s[r] : fill;
   }
 }
 
@@ -371,34 +370,74 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(const BwdParams
     const bool pre = t + 2 < ntl;
     if (pre) issue(nxt, t + 2);
     const int j0 = bt.j0(t);
-    // two halves of 32 keys: S^T, dP^T, then dQ^T over those keys
+    const bool whole = kt.whole(j0);
+    // Two halves of 32 keys in four runs of products, the order fixed by
+    // scheduling barriers and each operand read issued four products ahead:
+    // S^T and dP^T of half 0; those of half 1 with the softmax of half 0
+    // between them; the masks (one branch: dS of half 0 -> 0, S^T of half 1
+    // -> -inf); dQ^T of half 0 with the softmax of half 1 between its
+    // products; dQ^T of half 1.
+    f32x16 sc[2], dp[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 sc, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sc[r] = 0.f;
-        dp[r] = 0.f;
-      }
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(to.row_op(ks, kb, c), qf[c], sc, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(to.row_op(vs, kb, c), gf[c], dp, 0, 0, 0);
-      }
-      mask_keys(p, sc, j0, kb, qpos, kt, h);
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], p.scale_log2, -lse2));
-        sc[r] = pr * (dp[r] - dsum);
+        sc[kb][r] = 0.f;
+        dp[kb][r] = 0.f;
       }
-      bf16x8 dsf[2];
-      pack_half(sc, dsf);
+    // dS = exp2(S·sigma·log2 e - LSE·log2 e) (dP - D) of register r of half kb, in place
+    auto soft = [&](int kb, int r) {
+      const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], p.scale_log2, -lse2));
+      sc[kb][r] = pr * (dp[kb][r] - dsum);
+    };
+    constexpr int NC = D / 16, NS = 2 * NC, AH = 4;
+    {
+      // product i of half kb: chunk i / 2, S^T (K rows) or dP^T (V rows)
+      auto rd = [&](int i) { return to.row_op((i % NS) & 1 ? vs : ks, i / NS, (i % NS) >> 1); };
+      bf16x8 a[2 * NS];
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int i = 0; i < AH; ++i) a[i] = rd(i);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-          dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(to.tr_op(ks, db, 2 * kb + k2), dsf[k2], dqacc[db],
-                                                              0, 0, 0);
+      for (int i = 0; i < 2 * NS; ++i) {
+        const int kb = i / NS, j = i % NS;
+        if (j & 1)
+          dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], gf[j >> 1], dp[kb], 0, 0, 0);
+        else
+          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], qf[j >> 1], sc[kb], 0, 0, 0);
+        if (i + AH < 2 * NS) a[i + AH] = rd(i + AH);
+        if (kb == 1) {
+#pragma unroll
+          for (int r = j * 16 / NS; r < (j + 1) * 16 / NS; ++r) soft(0, r);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (!whole) {
+      mask_keys(p, sc[0], j0, 0, qpos, h, 0.f);
+      mask_keys(p, sc[1], j0, 1, qpos, h, -INFINITY);
+    }
+    {
+      // product i: 16-key slice 2kb + i / ND of the K tile, d-block i % ND
+      constexpr int ND = D / 32, NQ = 2 * ND;
+      auto rd = [&](int i) { return to.tr_op(ks, (i % NQ) % ND, 2 * (i / NQ) + (i % NQ) / ND); };
+      bf16x8 a[2 * NQ], dsf[2][2];
+      pack_half(sc[0], dsf[0]);
+#pragma unroll
+      for (int i = 0; i < AH; ++i) a[i] = rd(i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 2 * NQ; ++i) {
+        const int kb = i / NQ, j = i % NQ;
+        if (i == NQ) pack_half(sc[1], dsf[1]);
+        dqacc[j % ND] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], dsf[kb][j / ND], dqacc[j % ND], 0, 0, 0);
+        if (i + AH < 2 * NQ) a[i + AH] = rd(i + AH);
+        if (kb == 0) {
+#pragma unroll
+          for (int r = j * 16 / NQ; r < (j + 1) * 16 / NQ; ++r) soft(1, r);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (pre)
       stage_barrier<kLoads>();
