@@ -22,22 +22,24 @@
 //    S^T = K·Q^T and dP^T = V·dO^T take row reads of the K and V tiles;
 //    P and dS are formed in the accumulator layout, and dQ^T += K^T·dS^T
 //    takes transposing reads of the same K tile.
-//  * bwd_dkdv, key-stationary: a wave keeps 16 keys' k~ and v in registers
-//    and walks the 64-row tiles of q~, dO and the row statistics of every
-//    query head of its KV head that keeps those keys.  S = Q·K^T and
-//    dP = dO·V^T take row reads; dV^T += dO^T·P and dK^T += Q^T·dS take
-//    transposing reads.  The G heads of the group are summed in registers,
-//    so every dk, dv row is written once (no atomics).  16 keys per wave on
-//    v_mfma_f32_16x16x32_bf16 keep the stationary state at 96 registers, so
-//    two waves share each SIMD (with 32 keys on 32x32x16 it took 460
-//    registers, one wave per SIMD, and nothing hid its softmax and latency).
-//  * The dq products are v_mfma_f32_32x32x16_bf16.  All products take bf16
-//    operands with fp32 accumulation: q~ and k~ come in bf16, and P and dS
-//    are rounded to bf16 (dS needs bf16's exponent range: its entries shrink
-//    with the row length).
-//  * Each kernel's tile swizzle serves both its row reads (one 16-byte chunk
-//    of each of 16 consecutive rows per 16 lanes) and its transposing reads
-//    without LDS bank conflicts.
+//  * bwd_dkdv, key-stationary: a pair of waves keeps 32 keys' k~ and v in
+//    registers and walks the 64-row tiles of q~, dO and the row statistics
+//    of every query head of its KV head that keeps those keys.  Each wave
+//    of the pair forms S = Q·K^T and dP = dO·V^T for half of the tile's rows
+//    (row reads), and after trading one bf16 operand with its partner
+//    through LDS one of them accumulates dV^T += dO^T·P, the other dK^T +=
+//    Q^T·dS over all 64 rows (transposing reads).  The G heads of the group
+//    are summed in registers, so every dk, dv row is written once (no
+//    atomics).  Every q~ / dO operand read feeds 32 keys, half the LDS
+//    traffic of 16 keys per wave, while each wave holds one 64-register
+//    accumulator, so two waves still share each SIMD.
+//  * All products are v_mfma_f32_32x32x16_bf16, bf16 operands with fp32
+//    accumulation: q~ and k~ come in bf16, and P and dS are rounded to bf16
+//    (dS needs bf16's exponent range: its entries shrink with the row
+//    length).
+//  * The tile swizzle serves both the row reads (one 16-byte chunk of each of
+//    16 consecutive rows per 16 lanes) and the transposing reads without LDS
+//    bank conflicts.
 //  * Tiles are copied global -> LDS with no register round trip, three
 //    stages deep, one barrier per step (as in the forward).
 #include "attn_tile.h"
@@ -60,31 +62,12 @@ __device__ __forceinline__ int b_swz(int r) {
 }
 
 // Copy of the 64-row tile at rows j0 .. j0+63 of a [rows][D] bf16 matrix
-// (row stride rs elements) into LDS, row r's chunk c in slot c ^ swz(r):
+// (row stride rs elements) into LDS, row r's chunk c in slot c ^ b_swz(r):
 // per wave LPW loads, lane L of load i fills row (wave·LPW + i)·RPL + L/CPR,
 // slot L % CPR.  The resource ends at the last existing row (rows past it
 // land as zeros) and spans at most one tile, so any row stride below 2^25
 // elements keeps offsets in 32 bits.
-// Tiles of the 16-key dK/dV kernel: its transposing reads take 2 chunks of 8
-// consecutive rows per 32 lanes (a wave's two halves are served in separate
-// passes), so (c ^ s_swz(r)) >> 1 differs over 8 consecutive rows.  For its
-// row reads (ds_read_b128, 16 rows x 4 chunks per wave) the bit of row 8
-// enters slot bit 2, not bit 0 (D = 128): among the swizzles that keep the
-// transposing reads clean, these are the ones the hardware's bank-conflict
-// counter reads as zero for both read patterns (the counter gave 4 conflict
-// cycles per row read with bit 0, and with the first form for d = 64).
-template <int D>
-__device__ __forceinline__ int s_swz(int r) {
-  return D == 128 ? (((r & 7) << 1) ^ (((r >> 3) & 1) << 2))
-                  : ((((r >> 1) & 1) << 2) ^ (((r >> 2) & 1) << 1) ^ (((r >> 3) & 1) << 2));
-}
-
-template <int D, bool S16>
-__device__ __forceinline__ int tile_swz(int r) {
-  return S16 ? s_swz<D>(r) : b_swz<D>(r);
-}
-
-template <int D, int NW, bool S16 = false>
+template <int D, int NW>
 struct TileCopy {
   static constexpr int CPR = D / 8;
   static constexpr int RPL = 1024 / (2 * D);
@@ -109,7 +92,7 @@ struct TileCopy {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int row = row0 + i * RPL + lane / CPR;
-      const uint32_t off = (uint32_t)row * rs2 + (uint32_t)(((lane % CPR) ^ tile_swz<D, S16>(row)) * 16);
+      const uint32_t off = (uint32_t)row * rs2 + (uint32_t)(((lane % CPR) ^ b_swz<D>(row)) * 16);
       lds_copy16(r, off, lds_addr + (uint32_t)((row0 + i * RPL) * D * 2));
     }
   }
@@ -286,8 +269,9 @@ struct KeptTiles {
 };
 
 // Key mask of half kb of a 64-key tile for the lane's query row (S^T
-// accumulator layout: register r is key kb·32 + (r/4)·8 + 4h + r%4); tiles
-// that every row of the wave keeps whole are left alone.  The lane's key
+// accumulator layout: register r is key kb·32 + (r/4)·8 + 4h + r%4): entries
+// outside it become `fill`; the caller skips tiles that every row of the
+// wave keeps whole.  The lane's key
 // offset is bias + c with c a constant of the unrolled loop: the bounds are
 // shifted by bias once and each element compares against an inline constant.
 __device__ __forceinline__ void mask_keys(const BwdParams& p, f32x16& s, int j0, int kb, int64_t qpos, int h,
@@ -508,34 +492,47 @@ __device__ __forceinline__ KeyBlock key_block(const BwdParams& p, int unit) {
   return kb;
 }
 
-// dK, dV on v_mfma_f32_16x16x32_bf16 with 16 keys per wave: the stationary
-// state (k~, v fragments and the dK^T, dV^T accumulators) is 96 registers for
-// d = 128, so two waves share each SIMD and hide each other's softmax and LDS
-// latency.  Layouts (lane l, i = l % 16, g = l / 16):
-//   A operand  lane holds A[i][8g .. 8g+7]
-//   B operand  lane holds B[8g .. 8g+7][i]
-//   C/D        register r of lane holds C[4g + r][i]
-// S = Q·K^T per 16-row block rb: A = q~ rows (row 16rb + i, chunk 4c + g),
-// B = k~ of key i; the accumulator gives key i, rows 16rb + 4g + r.  The B
-// operand of dV^T += dO^T·P over the 32 rows of half kc is then registers
-// 0-3 of blocks 2kc and 2kc+1: rows 32kc + 4g + {0..3} and 32kc + 16 + 4g +
-// {0..3}; the A operand dO^T holds the same rows of column 16db + i, two
-// transposing reads (lane j of group g reads row 32kc + 4g + j/4, and 16
-// below, columns 16db + 4(j % 4) .. +3).
+// dK, dV with pairs of waves on v_mfma_f32_32x32x16_bf16: the two waves of
+// pair w/2 hold the same 32 keys (k~ and v as B operands, as in dq) and
+// split each 64-row step: role 0 (even wave) forms S and dP of tile rows
+// 0-31, role 1 of rows 32-63.  Role 0 accumulates dV^T += dO^T·P over all
+// 64 rows and role 1 dK^T += Q^T·dS, so role 0 hands its dS rows and role 1
+// its P rows to the partner through LDS (2 KB per wave and step, one buffer
+// per step parity).  Every q~ / dO operand read feeds 32 keys, and each
+// wave's accumulator is one of dK^T, dV^T (64 registers at d = 128), so two
+// waves share each SIMD.
+// Layouts (32x32x16; lane l, n = l % 32, h = l / 32): A lane holds
+// A[n][8h .. 8h+7], B lane holds B[8h .. 8h+7][n], register r of C holds
+// C[8(r/4) + 4h + r%4][n].  S = Q·K^T: A = q~ rows of the role's half
+// (TileOffsets row reads), B = k~ of key n; the accumulator gives key n,
+// rows 8j + 4h + {0..3}, whose two 16-row slices are the B operands of the
+// products over rows (pack_half), matched by the transposing reads of dO^T
+// and q~^T (TileOffsets transposing offsets).
+// A step: the S products, then the dP products with the exponentials of S
+// between them (the row statistics start the accumulators); dS, the partner's slices into buffer s % 2, one barrier, the
+// copy of tile s + 2 into the stage of tile s - 1 (every wave finished with
+// it before the barrier), the partner's slices read back and the 16
+// products over rows.  Buffer s % 2 is written again at step s + 2, after
+// the barrier of step s + 1, which the partner passes only after its reads
+// of step s.  Each operand read is issued AH products ahead (scheduling
+// barriers fix the order).
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p) {
-  using C = TileCopy<D, NW, true>;
+  using C = TileCopy<D, NW>;
   constexpr int TE = BN * D;
   constexpr int SE = StatsCopy1::FLOATS;
-  __shared__ __attribute__((aligned(1024))) uint16_t q_st[3][TE];
-  __shared__ __attribute__((aligned(1024))) uint16_t g_st[3][TE];
+  constexpr int AH = 4;
+  // stage st: q~ tile at t_st[st][0], dO tile at t_st[st][1]
+  __shared__ __attribute__((aligned(1024))) uint16_t t_st[3][2][TE];
   __shared__ __attribute__((aligned(1024))) float s_st[3][SE];
+  __shared__ __attribute__((aligned(1024))) uint16_t x_st[2][NW][2][64 * 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int i16 = lane & 15;
-  const int g = lane >> 4;
+  const int role = wave & 1;
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
 
   __shared__ int unit_slot;
   const int unit = workgroup_unit(p.sched, &unit_slot);
@@ -543,69 +540,57 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
   const KeyBlock kb = key_block<16 * NW>(p, unit);
   const int nrt = kb.t_hi - kb.t_lo;
   const int nsteps = nrt * p.G;
-  const int64_t wkey0 = kb.key0 + 16 * wave;
-  const int64_t key = wkey0 + i16;
+  const int64_t wkey0 = kb.key0 + 32 * (wave >> 1);
+  const int64_t key = wkey0 + l32;
   const bool kvalid = key < p.n_kv;
   const int64_t kpos = p.k_pos0 + key;
 
-  // B operands of S and dP: key i16's elements 32c + 8g .. +7
-  bf16x8 kf[D / 32], vf[D / 32];
-  {
-    const uint16_t* kbase = p.k + kb.b * p.ks_b + kb.hkv * p.ks_h + key * p.ks_s;
-    const uint16_t* vbase = p.v + kb.b * p.vs_b + kb.hkv * p.vs_h + key * p.vs_s;
+  bf16x8 kf[D / 16], vf[D / 16];
+  load_frag<D>(p.k + kb.b * p.ks_b + kb.hkv * p.ks_h, key, kvalid, p.ks_s, h, kf);
+  load_frag<D>(p.v + kb.b * p.vs_b + kb.hkv * p.vs_h, key, kvalid, p.vs_s, h, vf);
+  // role 0: dV^T, role 1: dK^T (register r of block db: d = 32db + 8(r/4) + 4h + r%4, key n)
+  f32x16 acc[D / 32];
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
-      u32x4 rk = {0u, 0u, 0u, 0u}, rv = {0u, 0u, 0u, 0u};
-      if (kvalid) {
-        rk = *reinterpret_cast<const u32x4*>(kbase + 32 * c + 8 * g);
-        rv = *reinterpret_cast<const u32x4*>(vbase + 32 * c + 8 * g);
-      }
-      kf[c] = __builtin_bit_cast(bf16x8, rk);
-      vf[c] = __builtin_bit_cast(bf16x8, rv);
-    }
-  }
-  f32x4 dkacc[D / 16], dvacc[D / 16];
+  for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      dkacc[db][r] = 0.f;
-      dvacc[db][r] = 0.f;
-    }
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
-  const bool keys_whole = wkey0 + 16 <= p.n_kv;
-  const int64_t wkpos_min = p.k_pos0 + wkey0, wkpos_max = wkpos_min + 15;
+  // row tiles (first row at query position q_pos0 + j0) whose rows R0 ..
+  // R0 + 31 all keep the pair's 32 keys: rt_lo <= j0 <= rt_hi, with the keys
+  // whole; the 64-bit tests once per wave (saturated to int32, which keeps
+  // every outcome for j0 in [0, 2^31 - 1)), 32-bit scalar compares per step
+  const int R0 = 32 * role;
+  const bool keys_whole = wkey0 + 32 <= p.n_kv;
+  const int64_t wkpos_min = p.k_pos0 + wkey0, wkpos_max = wkpos_min + 31;
   const bool k_sink = kpos < (int64_t)p.n_sink;
-  // row tiles (first row at query position q_pos0 + j0) whose 64 rows all
-  // keep the wave's 16 keys: rt_lo <= j0 <= rt_hi, with the keys whole; the
-  // 64-bit tests once per wave (saturated to int32, which keeps every outcome
-  // for j0 in [0, 2^31 - 1)), 32-bit scalar compares per step
   int rt_lo, rt_hi;
   {
-    int64_t h = p.n_q - BN;  // j0 + BN <= n_q
+    int64_t hh = p.n_q - R0 - 32;  // j0 + R0 + 32 <= n_q
     if (p.window >= 0 && !(wkpos_max < (int64_t)p.n_sink)) {
-      // q_pos0 + j0 + BN - 1 - window <= wkpos_min
-      const int64_t w = wkpos_min + p.window - p.q_pos0 - (BN - 1);
-      h = h < w ? h : w;
+      // q_pos0 + j0 + R0 + 31 - window <= wkpos_min
+      const int64_t w = wkpos_min + p.window - p.q_pos0 - R0 - 31;
+      hh = hh < w ? hh : w;
     }
-    rt_hi = KeptTiles::sat(h);
-    rt_lo = p.causal ? KeptTiles::sat(wkpos_max - p.q_pos0) : INT32_MIN;  // q_pos0 + j0 >= wkpos_max
-  }
-
-  // per-lane LDS offsets: row reads and the first transposing read
-  int roff[D / 32], toff[D / 16];
-#pragma unroll
-  for (int c = 0; c < D / 32; ++c) roff[c] = i16 * D + 8 * ((4 * c + g) ^ s_swz<D>(i16));
-  {
-    const int r0 = 4 * g + (i16 >> 2);
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db)
-      toff[db] = r0 * D + 8 * ((2 * db + ((i16 & 3) >> 1)) ^ s_swz<D>(r0)) + 4 * (i16 & 1);
+    rt_hi = KeptTiles::sat(hh);
+    rt_lo = p.causal ? KeptTiles::sat(wkpos_max - p.q_pos0 - R0) : INT32_MIN;  // q_pos0 + j0 + R0 >= wkpos_max
   }
 
   C qcp, gcp;
   qcp.init(p.qs_s, wave, lane);
   gcp.init(p.dos_s, wave, lane);
+  // lane offsets into a stage: row reads of the role's 32 rows (q~; dO at
+  // + TE), transposing reads of dO (role 0) or q~ (role 1)
+  int roff[D / 16], toff[2][D / 32];
+  {
+    TileOffsets<D> to;
+    to.init(lane);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) roff[c] = to.roff[c] + R0 * D;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) toff[hf][db] = to.toff[hf][db] + (role ? 0 : TE);
+  }
   // Copy sources of the next step to issue (row tile it, head hkv·G + ig),
   // advanced per issue: steps run over the G heads of a row tile, then the
   // row tile above (no divisions, pointers moved by their strides)
@@ -617,14 +602,13 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
   const int64_t q_wrap = (int64_t)(p.G - 1) * p.qs_h + (int64_t)BN * p.qs_s;
   const int64_t g_wrap = (int64_t)(p.G - 1) * p.dos_h + (int64_t)BN * p.dos_s;
   const int64_t s_wrap = 2 * ((int64_t)(p.G - 1) * p.n_q + BN);
-  const uint32_t lq = (uint32_t)(uintptr_t)(lds_void*)&q_st[0][0];
-  const uint32_t lg = (uint32_t)(uintptr_t)(lds_void*)&g_st[0][0];
+  const uint32_t lt = (uint32_t)(uintptr_t)(lds_void*)&t_st[0][0][0];
   const uint32_t ls = (uint32_t)(uintptr_t)(lds_void*)&s_st[0][0];
   auto issue_next = [&](int st) {
     const int left = (int)p.n_q - it * BN;  // n_q < 2^31
     const uint32_t rows = left <= 0 ? 0u : (left >= BN ? (uint32_t)BN : (uint32_t)left);
-    qcp.issue_rows(lq + (uint32_t)(st * TE * 2), iq, rows);
-    gcp.issue_rows(lg + (uint32_t)(st * TE * 2), igo, rows);
+    qcp.issue_rows(lt + (uint32_t)(st * 2 * TE * 2), iq, rows);
+    gcp.issue_rows(lt + (uint32_t)((st * 2 + 1) * TE * 2), igo, rows);
     // the statistics come with wave 0's copies (one 512-byte load instead
     // of one small load per wave)
     if (wave == 0) StatsCopy1::issue_rows(ls + (uint32_t)(st * SE * 4), ist, rows, lane);
@@ -640,202 +624,165 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
       ist += 2 * p.n_q;
     }
   };
-  constexpr int kLoads = 2 * C::LPW;  // vector memory ops per step (wave 0: one more)
+
+  // statistics of the step's rows R0 + 8j + 4h + {0..3}: 8 consecutive
+  // floats each (LSE·log2 e, D)
+  float l2n[16], ddn[16];
+  const float inv_sl2 = 1.f / p.scale_log2;
+  auto load_stats = [&](int st) {
+    const float* sr = s_st[st] + 2 * (R0 + 4 * h);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 ta = *reinterpret_cast<const f32x4*>(sr + 16 * j);
+      const f32x4 tc = *reinterpret_cast<const f32x4*>(sr + 16 * j + 4);
+      l2n[4 * j] = ta[0];
+      ddn[4 * j] = ta[1];
+      l2n[4 * j + 1] = ta[2];
+      ddn[4 * j + 1] = ta[3];
+      l2n[4 * j + 2] = tc[0];
+      ddn[4 * j + 2] = tc[1];
+      l2n[4 * j + 3] = tc[2];
+      ddn[4 * j + 3] = tc[3];
+    }
+  };
 
   int ct = kb.t_hi - 1, cg = 0;  // row tile and head of the step
-  auto step = [&](const uint16_t* qs, const uint16_t* gs, const float* ss, int nxt, int s) {
-    const bool pre = s + 2 < nsteps;
-    if (pre) issue_next(nxt);
+  auto step = [&](int cur, int nxt, int s) {
+    const uint16_t* ts = t_st[cur][0];
     const int j0 = ct * BN;
     if (++cg == p.G) {
       cg = 0;
       --ct;
     }
     const bool all_kept = keys_whole && j0 >= rt_lo && j0 <= rt_hi;
-    // The step in four runs of 16 products, each operand read issued four
-    // products ahead and the order fixed by scheduling barriers: S and dP of
-    // rows 0-31 (half 0); S and dP of half 1 with the softmax of half 0
-    // between the products; the masks (one branch); dV^T and dK^T of half 0
-    // with the softmax of half 1 between them; dV^T and dK^T of half 1.  The
-    // exponentials and the products of the other half then share the SIMD
-    // instead of taking turns.
-    f32x4 sc[2][2], dp[2][2];  // [half kc][row block u]
+    load_stats(cur);
+    // products 0 .. D/16-1: S (q~ rows, k~) from -LSE·log2 e / (sigma·log2 e),
+    // so that P = exp2(S'·sigma·log2 e); then dP (dO rows, v) from -D, with
+    // the exponentials between them
+    constexpr int NC = D / 16, NA = 2 * NC, VP = 16 / NC;
+    f32x16 sc, dp;
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          sc[kc][u][r] = 0.f;
-          dp[kc][u][r] = 0.f;
-        }
-    // statistics of the lane's rows 32kc + 16u + 4g + {0..3}: LSE·log2 e, D
-    float l2[2][2][4], dd[2][2][4];
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int row = 32 * kc + 16 * u + 4 * g;
-        const f32x4 ta = *reinterpret_cast<const f32x4*>(ss + 2 * row);
-        const f32x4 tc = *reinterpret_cast<const f32x4*>(ss + 2 * row + 4);
-        l2[kc][u][0] = ta[0];
-        dd[kc][u][0] = ta[1];
-        l2[kc][u][1] = ta[2];
-        dd[kc][u][1] = ta[3];
-        l2[kc][u][2] = tc[0];
-        dd[kc][u][2] = tc[1];
-        l2[kc][u][3] = tc[2];
-        dd[kc][u][3] = tc[3];
-      }
-    // P = exp2(S·sigma·log2 e - LSE·log2 e) and dS = P (dP - D) of value v
-    // (row block v / 4, register v % 4) of half kc, in place
-    auto soft = [&](int kc, int v) {
-      const int u = v >> 2, r = v & 3;
-      const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kc][u][r], p.scale_log2, -l2[kc][u][r]));
-      sc[kc][u][r] = pr;
-      dp[kc][u][r] = pr * (dp[kc][u][r] - dd[kc][u][r]);
-    };
-    // S / dP products: i -> chunk c = i / 4, row block u = (i / 2) % 2, S or dP
-    constexpr int NS = 4 * (D / 32);
-    auto rd_s = [&](int kc, int i) {
-      const int c = i >> 2, u = (i >> 1) & 1, rb = 2 * kc + u;
-      return *reinterpret_cast<const bf16x8*>((i & 1 ? gs : qs) + rb * 16 * D + roff[c]);
-    };
-    auto mfma_s = [&](int kc, int i, const bf16x8& a) {
-      const int c = i >> 2, u = (i >> 1) & 1;
-      if (i & 1)
-        dp[kc][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, vf[c], dp[kc][u], 0, 0, 0);
-      else
-        sc[kc][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kf[c], sc[kc][u], 0, 0, 0);
-    };
-    {
-      constexpr int AH = 4;
-      bf16x8 a[2 * NS];
-#pragma unroll
-      for (int i = 0; i < AH; ++i) a[i] = rd_s(0, i);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < 2 * NS; ++i) {
-        mfma_s(i / NS, i % NS, a[i]);
-        if (i + AH < 2 * NS) a[i + AH] = rd_s((i + AH) / NS, (i + AH) % NS);
-        if (i >= NS) {
-#pragma unroll
-          for (int v = (i - NS) * 8 / NS; v < (i - NS + 1) * 8 / NS; ++v) soft(0, v);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int r = 0; r < 16; ++r) {
+      sc[r] = -l2n[r] * inv_sl2;
+      dp[r] = -ddn[r];
     }
-    // element (kc, u, r) is row 32kc + 16u + 4g + r of the tile and the lane's
-    // key; half 0 holds P and dS already (its pairs outside the mask become
-    // 0, whatever their exponential gave), half 1 still S
+    bf16x8 a[NA];
+    auto rd = [&](int i) {
+      return *reinterpret_cast<const bf16x8*>(ts + roff[i % NC] + (i < NC ? 0 : TE));
+    };
+#pragma unroll
+    for (int i = 0; i < AH; ++i) a[i] = rd(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      if (i < NC) {
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], kf[i], sc, 0, 0, 0);
+      } else {
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], vf[i - NC], dp, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < VP; ++v) {
+          const int r = (i - NC) * VP + v;
+          sc[r] = __builtin_amdgcn_exp2f(sc[r] * p.scale_log2);
+        }
+      }
+      if (i + AH < NA) a[i + AH] = rd(i + AH);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // register r: row R0 + 4h + c of the tile with c = 8(r/4) + r%4, key l32;
+    // P of a pair outside the mask is 0 (its exponential may have overflowed)
     if (!all_kept) {
       const int64_t qpos_t = p.q_pos0 + j0;
       const int hi = clamp_i32(qpos_t - kpos);  // causal: row off kept iff hi + off >= 0
       const int lo = p.window >= 0 ? clamp_i32(qpos_t - kpos - p.window) : -(1 << 30);  // lo + off <= 0
-      const int rrem = clamp_tile(p.n_q - (int64_t)j0);
+      const int bias = R0 + 4 * h;
+      const int a_r = clamp_tile(p.n_q - (int64_t)j0) - bias, a_hi = hi + bias, a_lo = lo + bias;
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int off = 32 * kc + 16 * u + 4 * g + r;
-            const bool ok = kvalid & (off < rrem) & (!p.causal | (hi + off >= 0)) & ((lo + off <= 0) | k_sink);
-            if (kc == 0) {
-              sc[0][u][r] = ok ? sc[0][u][r] : 0.f;
-              dp[0][u][r] = ok ? dp[0][u][r] : 0.f;
-            } else {
-              sc[1][u][r] = ok ? sc[1][u][r] : -INFINITY;
-            }
-          }
-    }
-    auto pack = [&](int kc, bf16x8& pf, bf16x8& dsf) {
-      u32x4 wp, wd;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        wp[2 * u] = pack_bf16x2(sc[kc][u][0], sc[kc][u][1]);
-        wp[2 * u + 1] = pack_bf16x2(sc[kc][u][2], sc[kc][u][3]);
-        wd[2 * u] = pack_bf16x2(dp[kc][u][0], dp[kc][u][1]);
-        wd[2 * u + 1] = pack_bf16x2(dp[kc][u][2], dp[kc][u][3]);
+      for (int r = 0; r < 16; ++r) {
+        const int c = (r >> 2) * 8 + (r & 3);
+        const bool ok = kvalid & (c < a_r) & (!p.causal | (a_hi + c >= 0)) & ((a_lo + c <= 0) | k_sink);
+        sc[r] = ok ? sc[r] : 0.f;
       }
-      pf = __builtin_bit_cast(bf16x8, wp);
-      dsf = __builtin_bit_cast(bf16x8, wd);
-    };
-    // dV^T += dO^T·P, dK^T += Q^T·dS over a half's 32 rows: i -> d-block
-    // db = i / 2, dV or dK
-    auto rd_t = [&](int kc, int i) {
-      const int o0 = toff[i >> 1] + kc * 32 * D;
-      const uint16_t* t = i & 1 ? qs : gs;
-      const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(t + o0));
-      const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(t + o0 + 16 * D));
+    }
+    // dS = P (dP - D)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dp[r] = sc[r] * dp[r];
+    bf16x8 pf[2], df[2], own[2];
+    pack_half(sc, pf);
+    pack_half(dp, df);
+    const int buf = s & 1;
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      own[k2] = role ? df[k2] : pf[k2];
+      *reinterpret_cast<bf16x8*>(&x_st[buf][wave][k2][lane * 8]) = role ? pf[k2] : df[k2];
+    }
+    stage_barrier<0>();
+    if (s + 2 < nsteps) issue_next(nxt);
+    // the 16-row slices of tile rows 0-31 (lo) and 32-63 (hi): one pair the
+    // wave's own, the other its partner's
+    bf16x8 b_lo[2], b_hi[2];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const bf16x8 part = *reinterpret_cast<const bf16x8*>(&x_st[buf][wave ^ 1][k2][lane * 8]);
+      b_lo[k2] = role ? part : own[k2];
+      b_hi[k2] = role ? own[k2] : part;
+    }
+    // role 0: dV^T += dO^T·P, role 1: dK^T += Q^T·dS; product i: 16-row
+    // slice i / ND, d-block i % ND
+    constexpr int ND = D / 32, NB = 4 * ND;
+    bf16x8 t[NB];
+    auto rt = [&](int i) {
+      const int kc = i / ND, db = i % ND;
+      const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(ts + toff[0][db] + kc * 16 * D));
+      const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(ts + toff[1][db] + kc * 16 * D));
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    constexpr int NT = 2 * (D / 16);
-    bf16x8 pf[2], dsf[2];
-    pack(0, pf[0], dsf[0]);
-    {
-      constexpr int AH = 4;
-      bf16x8 a[2 * NT];
 #pragma unroll
-      for (int i = 0; i < AH; ++i) a[i] = rd_t(0, i);
+    for (int i = 0; i < AH; ++i) t[i] = rt(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int kc = i / ND;
+      const bf16x8 b = kc < 2 ? b_lo[kc] : b_hi[kc - 2];
+      acc[i % ND] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t[i], b, acc[i % ND], 0, 0, 0);
+      if (i + AH < NB) t[i + AH] = rt(i + AH);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < 2 * NT; ++i) {
-        const int kc = i / NT, j = i % NT;
-        if (i == NT) pack(1, pf[1], dsf[1]);
-        if (j & 1)
-          dkacc[j >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], dsf[kc], dkacc[j >> 1], 0, 0, 0);
-        else
-          dvacc[j >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], pf[kc], dvacc[j >> 1], 0, 0, 0);
-        if (i + AH < 2 * NT) a[i + AH] = rd_t((i + AH) / NT, (i + AH) % NT);
-        if (i < NT) {
-#pragma unroll
-          for (int v = i * 8 / NT; v < (i + 1) * 8 / NT; ++v) soft(1, v);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
     }
-    if (!pre)
-      stage_barrier<0>();
-    else if (wave == 0)
-      stage_barrier<kLoads + 1>();
-    else
-      stage_barrier<kLoads>();
   };
 
   if (nsteps > 0) issue_next(0);
   if (nsteps > 1) issue_next(1);
   stage_barrier<0>();
+  // tile s is in stage s % 3; tile s + 2 goes to stage (s + 2) % 3
   int cur = 0, nxt = 2;
   for (int s = 0; s < nsteps; ++s) {
-    step(q_st[cur], g_st[cur], s_st[cur], nxt, s);
+    step(cur, nxt, s);
     cur = cur == 2 ? 0 : cur + 1;
     nxt = nxt == 2 ? 0 : nxt + 1;
   }
 
   if (!kvalid) return;
-  void* dkd;
-  void* dvd;
-  if (p.grad_f32) {
-    dkd = static_cast<float*>(p.dk) + kb.b * p.dks_b + kb.hkv * p.dks_h + key * p.dks_s;
-    dvd = static_cast<float*>(p.dv) + kb.b * p.dvs_b + kb.hkv * p.dvs_h + key * p.dvs_s;
-  } else {
-    dkd = static_cast<uint16_t*>(p.dk) + kb.b * p.dks_b + kb.hkv * p.dks_h + key * p.dks_s;
-    dvd = static_cast<uint16_t*>(p.dv) + kb.b * p.dvs_b + kb.hkv * p.dvs_h + key * p.dvs_s;
-  }
+  const bool is_dk = role != 0;
+  void* dst;
+  if (p.grad_f32)
+    dst = is_dk ? (void*)(static_cast<float*>(p.dk) + kb.b * p.dks_b + kb.hkv * p.dks_h + key * p.dks_s)
+                : (void*)(static_cast<float*>(p.dv) + kb.b * p.dvs_b + kb.hkv * p.dvs_h + key * p.dvs_s);
+  else
+    dst = is_dk ? (void*)(static_cast<uint16_t*>(p.dk) + kb.b * p.dks_b + kb.hkv * p.dks_h + key * p.dks_s)
+                : (void*)(static_cast<uint16_t*>(p.dv) + kb.b * p.dvs_b + kb.hkv * p.dvs_h + key * p.dvs_s);
+  const float f = is_dk ? p.scale : 1.f;
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db) {
-    const int d0 = db * 16 + g * 4;
-    const f32x4 xk = {dkacc[db][0] * p.scale, dkacc[db][1] * p.scale, dkacc[db][2] * p.scale,
-                      dkacc[db][3] * p.scale};
-    store4(p, dkd, kpos, d0, xk, p.unrotate != 0);
-    store4(p, dvd, kpos, d0, dvacc[db], false);
-  }
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 x = {acc[db][4 * r4] * f, acc[db][4 * r4 + 1] * f, acc[db][4 * r4 + 2] * f,
+                       acc[db][4 * r4 + 3] * f};
+      store4(p, dst, kpos, db * 32 + r4 * 8 + h * 4, x, is_dk && p.unrotate != 0);
+    }
 }
 
 constexpr int kBwdNWq128 = 8;  // dq kernel waves (32 rows each)
 constexpr int kBwdNWq64 = 4;
-constexpr int kBwdNWk = 8;     // dk/dv kernel waves (16 keys each)
+constexpr int kBwdNWk = 8;     // dk/dv kernel waves (pairs of waves on 32 keys)
 
 template __global__ void bwd_stats_kernel<64>(const BwdParams);
 template __global__ void bwd_stats_kernel<128>(const BwdParams);
