@@ -789,15 +789,23 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
                   const uint16_t* kls, uint16_t* kls_next, int t) {
     const int tn = t + NST - 1;
     const bool pre = tn < ntl;
-    if (pre) {
-      if constexpr (KMODE != 0) kreg.load(bt.j0(tn));
-      issue(ks_next, vs_next, tn);
+    if constexpr (KMODE != 0) {
+      if (pre) {
+        kreg.load(bt.j0(tn));
+        issue(ks_next, vs_next, tn);
+      }
     }
     f32x16 s_cur[2];
     if constexpr (PRECISE)
       qk_tile_precise<D>(ks, kls, koff, qf, qlo, rows.qk_init(), s_cur);
     else
       qk_tile<D>(ks, koff, qf, rows.qk_init(), s_cur);
+    // copies straight to LDS are issued after the QK^T products, so that the
+    // first operand reads follow the barrier without the copies' scalar work
+    // in front of them
+    if constexpr (KMODE == 0) {
+      if (pre) issue(ks_next, vs_next, tn);
+    }
     rows.mask(p, s_cur, bt.j0(t), h2);
     rows.rescale(rows.tile_max(s_cur), s_cur);
     u32x4 pf[4];
