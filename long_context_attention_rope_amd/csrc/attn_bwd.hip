@@ -352,7 +352,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(const BwdParams
   };
   auto step = [&](const uint16_t* ks, const uint16_t* vs, int nxt, int t) {
     const bool pre = t + 2 < ntl;
-    if (pre) issue(nxt, t + 2);
     const int j0 = bt.j0(t);
     const bool whole = kt.whole(j0);
     // Two halves of 32 keys in four runs of products, the order fixed by
@@ -397,6 +396,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(const BwdParams
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    // the copy of tile t + 2 after the first product run, so that the first
+    // operand reads follow the barrier without its scalar work
+    if (pre) issue(nxt, t + 2);
     if (!whole) {
       mask_keys(p, sc[0], j0, 0, qpos, h, 0.f);
       mask_keys(p, sc[1], j0, 1, qpos, h, -INFINITY);
@@ -509,10 +511,11 @@ __device__ __forceinline__ KeyBlock key_block(const BwdParams& p, int unit) {
 // products over rows (pack_half), matched by the transposing reads of dO^T
 // and q~^T (TileOffsets transposing offsets).
 // A step: the S products, then the dP products with the exponentials of S
-// between them (the row statistics start the accumulators); dS, the partner's slices into buffer s % 2, one barrier, the
-// copy of tile s + 2 into the stage of tile s - 1 (every wave finished with
-// it before the barrier), the partner's slices read back and the 16
-// products over rows.  Buffer s % 2 is written again at step s + 2, after
+// between them (the row statistics start the accumulators); dS, the
+// partner's slices into buffer s % 2, one barrier, the partner's slices read
+// back and the 16 products over rows, with the copy of tile s + 2 into the
+// stage of tile s - 1 (every wave finished with it before the barrier)
+// issued after the fourth of them.  Buffer s % 2 is written again at step s + 2, after
 // the barrier of step s + 1, which the partner passes only after its reads
 // of step s.  Each operand read is issued AH products ahead (scheduling
 // barriers fix the order).
@@ -716,7 +719,6 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
       *reinterpret_cast<bf16x8*>(&x_st[buf][wave][k2][lane * 8]) = role ? pf[k2] : df[k2];
     }
     stage_barrier<0>();
-    if (s + 2 < nsteps) issue_next(nxt);
     // the 16-row slices of tile rows 0-31 (lo) and 32-63 (hi): one pair the
     // wave's own, the other its partner's
     bf16x8 b_lo[2], b_hi[2];
@@ -746,6 +748,9 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
       acc[i % ND] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t[i], b, acc[i % ND], 0, 0, 0);
       if (i + AH < NB) t[i + AH] = rt(i + AH);
       __builtin_amdgcn_sched_barrier(0);
+      // the copy of tile s + 2 once the first products are issued (not
+      // between the barrier and the first operand reads)
+      if (i == 3 && s + 2 < nsteps) issue_next(nxt);
     }
   };
 
