@@ -332,8 +332,10 @@ typedef struct {
   void* dv;                 /* query heads of each KV head) */
   int32_t grad_dtype;       /* LCX_F32 or LCX_BF16 */
   int64_t dq_strides[3], dk_strides[3], dv_strides[3]; /* elements */
-  float* workspace;         /* fp32 [B][Hq][n_q][2], contiguous, 16-byte aligned, caller-owned
-                               scratch (per-row LSE·log2 e and D = <dO, O>) */
+  float* workspace;         /* fp32, 2·B·Hq·n_q floats (e.g. [B][Hq][n_q][2]), contiguous,
+                               16-byte aligned, caller-owned scratch, overwritten: per-row
+                               statistics of the forward's softmax (from lse) and
+                               D = <dO, O>, in a layout internal to the library */
   void* sched;              /* optional, LCX_SCHED_BYTES, 8-byte aligned, caller-owned,
                                overwritten: the dynamic work order of the dq and dk/dv
                                kernels, as lcx_attn_args.sched; NULL: static order */

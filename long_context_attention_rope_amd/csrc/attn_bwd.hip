@@ -16,7 +16,9 @@
 // "上下文窗口扩展技术：从 4K 到 1M" §4.1-§4.2 (window and sink mask).
 //
 // Design (CDNA4, wave64), three launches:
-//  * bwd_stats: per query row (LSE·log2 e, D) into an fp32 workspace.
+//  * bwd_stats: per query row -LSE/sigma and -D into two planes of an fp32
+//    workspace (plane stride B·Hq·n_q floats): the starts of the S and dP
+//    accumulators in the dk/dv kernel.
 //  * bwd_dq, query-stationary (the forward's shape): a wave keeps 32 rows'
 //    q~ and dO in registers and walks the forward's 64-key tiles.
 //    S^T = K·Q^T and dP^T = V·dO^T take row reads of the K and V tiles;
@@ -98,14 +100,20 @@ struct TileCopy {
   }
 };
 
-// Row statistics of a 64-row tile copied by one wave: 64 rows x 8 bytes,
-// lanes 0-31 in range (lanes past the last row land as zeros); row r at
-// float offset 2r.
+// Row statistics of a 64-row tile copied by one wave, one copy per plane:
+// 64 rows x 4 bytes each, lanes 0-15 in range (lanes past the last row land
+// as zeros); plane 0 (-LSE/sigma) of row r at float offset r, plane 1 (-D)
+// at PLANE1 + r.
 struct StatsCopy1 {
-  static constexpr int FLOATS = 256;  // LDS floats per stage (64 lanes x 16 B)
-  // from the statistics of the tile's first row (rows of them in range)
-  __device__ static __forceinline__ void issue_rows(uint32_t lds_addr, const float* first, uint32_t rows, int lane) {
-    lds_copy16(make_rsrc(first, __builtin_amdgcn_readfirstlane(rows * 8u)), (uint32_t)lane * 16u, lds_addr);
+  static constexpr int PLANE1 = 256;       // LDS floats per copy (64 lanes x 16 B)
+  static constexpr int FLOATS = 2 * PLANE1;  // LDS floats per stage
+  // from the statistics of the tile's first row (rows of them in range);
+  // pstride: floats from plane 0 to plane 1
+  __device__ static __forceinline__ void issue_rows(uint32_t lds_addr, const float* first, int64_t pstride,
+                                                    uint32_t rows, int lane) {
+    const uint32_t bytes = __builtin_amdgcn_readfirstlane(rows * 4u);
+    lds_copy16(make_rsrc(first, bytes), (uint32_t)lane * 16u, lds_addr);
+    lds_copy16(make_rsrc(first + pstride, bytes), (uint32_t)lane * 16u, lds_addr + PLANE1 * 4u);
   }
 };
 
@@ -238,9 +246,9 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(const BwdParams p) {
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m);
   if (grow < nrows && tid % LPR == 0) {
-    // an empty row (LSE = -inf) gets +inf, so that every P of it is 0
-    const f32x2 st = {lse == -INFINITY ? INFINITY : lse * kLog2e, acc};
-    *reinterpret_cast<f32x2*>(p.stats + 2 * grow) = st;
+    // an empty row (LSE = -inf) gets -inf, so that every P of it is 0
+    p.stats[grow] = lse == -INFINITY ? -INFINITY : -lse / p.scale;
+    p.stats[nrows + grow] = -acc;
   }
 }
 
@@ -322,9 +330,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(const BwdParams
   bf16x8 qf[D / 16], gf[D / 16];
   load_frag<D>(p.q + bt.b * p.qs_b + bt.hq * p.qs_h, qi, qvalid, p.qs_s, h, qf);
   load_frag<D>(p.dout + bt.b * p.dos_b + bt.hq * p.dos_h, qi, qvalid, p.dos_s, h, gf);
-  f32x2 st = {INFINITY, 0.f};  // rows past the end: every P is 0
-  if (qvalid) st = *reinterpret_cast<const f32x2*>(p.stats + 2 * (((int64_t)bt.b * p.Hq + bt.hq) * p.n_q + qi));
-  const float lse2 = st[0], dsum = st[1];
+  // LSE·log2 e and D of the lane's row (rows past the end: every P is 0)
+  float lse2 = INFINITY, dsum = 0.f;
+  if (qvalid) {
+    const int64_t row = ((int64_t)bt.b * p.Hq + bt.hq) * p.n_q + qi;
+    const float ml = p.stats[row];  // -LSE/sigma, -inf for an empty row
+    lse2 = ml == -INFINITY ? INFINITY : -ml * p.scale_log2;
+    dsum = -p.stats[(int64_t)p.B * p.Hq * p.n_q + row];
+  }
 
   f32x16 dqacc[D / 32];
 #pragma unroll
@@ -601,10 +614,11 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
   const int64_t hq0 = (int64_t)kb.hkv * p.G;
   const uint16_t* iq = p.q + kb.b * p.qs_b + hq0 * p.qs_h + (int64_t)it * BN * p.qs_s;
   const uint16_t* igo = p.dout + kb.b * p.dos_b + hq0 * p.dos_h + (int64_t)it * BN * p.dos_s;
-  const float* ist = p.stats + 2 * (((int64_t)kb.b * p.Hq + hq0) * p.n_q + (int64_t)it * BN);
+  const float* ist = p.stats + (((int64_t)kb.b * p.Hq + hq0) * p.n_q + (int64_t)it * BN);
+  const int64_t pstride = (int64_t)p.B * p.Hq * p.n_q;
   const int64_t q_wrap = (int64_t)(p.G - 1) * p.qs_h + (int64_t)BN * p.qs_s;
   const int64_t g_wrap = (int64_t)(p.G - 1) * p.dos_h + (int64_t)BN * p.dos_s;
-  const int64_t s_wrap = 2 * ((int64_t)(p.G - 1) * p.n_q + BN);
+  const int64_t s_wrap = (int64_t)(p.G - 1) * p.n_q + BN;
   const uint32_t lt = (uint32_t)(uintptr_t)(lds_void*)&t_st[0][0][0];
   const uint32_t ls = (uint32_t)(uintptr_t)(lds_void*)&s_st[0][0];
   auto issue_next = [&](int st) {
@@ -614,7 +628,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
     gcp.issue_rows(lt + (uint32_t)((st * 2 + 1) * TE * 2), igo, rows);
     // the statistics come with wave 0's copies (one 512-byte load instead
     // of one small load per wave)
-    if (wave == 0) StatsCopy1::issue_rows(ls + (uint32_t)(st * SE * 4), ist, rows, lane);
+    if (wave == 0) StatsCopy1::issue_rows(ls + (uint32_t)(st * SE * 4), ist, pstride, rows, lane);
     if (++ig == p.G) {
       ig = 0;
       --it;
@@ -624,28 +638,24 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
     } else {
       iq += p.qs_h;
       igo += p.dos_h;
-      ist += 2 * p.n_q;
+      ist += p.n_q;
     }
   };
 
-  // statistics of the step's rows R0 + 8j + 4h + {0..3}: 8 consecutive
-  // floats each (LSE·log2 e, D)
-  float l2n[16], ddn[16];
-  const float inv_sl2 = 1.f / p.scale_log2;
+  // accumulator starts of the step's rows R0 + 8j + 4h + {0..3} (register
+  // 4j .. 4j+3): -LSE/sigma for S, -D for dP, 16 bytes of each plane per j
+  f32x16 sc0, dp0;
   auto load_stats = [&](int st) {
-    const float* sr = s_st[st] + 2 * (R0 + 4 * h);
+    const float* sr = s_st[st] + R0 + 4 * h;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const f32x4 ta = *reinterpret_cast<const f32x4*>(sr + 16 * j);
-      const f32x4 tc = *reinterpret_cast<const f32x4*>(sr + 16 * j + 4);
-      l2n[4 * j] = ta[0];
-      ddn[4 * j] = ta[1];
-      l2n[4 * j + 1] = ta[2];
-      ddn[4 * j + 1] = ta[3];
-      l2n[4 * j + 2] = tc[0];
-      ddn[4 * j + 2] = tc[1];
-      l2n[4 * j + 3] = tc[2];
-      ddn[4 * j + 3] = tc[3];
+      const f32x4 ta = *reinterpret_cast<const f32x4*>(sr + 8 * j);
+      const f32x4 tc = *reinterpret_cast<const f32x4*>(sr + StatsCopy1::PLANE1 + 8 * j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sc0[4 * j + e] = ta[e];
+        dp0[4 * j + e] = tc[e];
+      }
     }
   };
 
@@ -659,16 +669,11 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
     }
     const bool all_kept = keys_whole && j0 >= rt_lo && j0 <= rt_hi;
     load_stats(cur);
-    // products 0 .. D/16-1: S (q~ rows, k~) from -LSE·log2 e / (sigma·log2 e),
-    // so that P = exp2(S'·sigma·log2 e); then dP (dO rows, v) from -D, with
-    // the exponentials between them
+    // products 0 .. D/16-1: S (q~ rows, k~) from -LSE/sigma, so that
+    // P = exp2(S'·sigma·log2 e); then dP (dO rows, v) from -D, with the
+    // exponentials between them
     constexpr int NC = D / 16, NA = 2 * NC, VP = 16 / NC;
-    f32x16 sc, dp;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sc[r] = -l2n[r] * inv_sl2;
-      dp[r] = -ddn[r];
-    }
+    f32x16 sc = sc0, dp = dp0;
     bf16x8 a[NA];
     auto rd = [&](int i) {
       return *reinterpret_cast<const bf16x8*>(ts + roff[i % NC] + (i < NC ? 0 : TE));
