@@ -528,7 +528,7 @@ __device__ __forceinline__ KeyBlock key_block(const BwdParams& p, int unit) {
 // partner's slices into buffer s % 2, one barrier, the partner's slices read
 // back and the 16 products over rows, with the copy of tile s + 2 into the
 // stage of tile s - 1 (every wave finished with it before the barrier)
-// issued after the fourth of them.  Buffer s % 2 is written again at step s + 2, after
+// issued after the last of them.  Buffer s % 2 is written again at step s + 2, after
 // the barrier of step s + 1, which the partner passes only after its reads
 // of step s.  Each operand read is issued AH products ahead (scheduling
 // barriers fix the order).
@@ -753,9 +753,10 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(const BwdParams p)
       acc[i % ND] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t[i], b, acc[i % ND], 0, 0, 0);
       if (i + AH < NB) t[i + AH] = rt(i + AH);
       __builtin_amdgcn_sched_barrier(0);
-      // the copy of tile s + 2 once the first products are issued (not
-      // between the barrier and the first operand reads)
-      if (i == 3 && s + 2 < nsteps) issue_next(nxt);
+      // the copy of tile s + 2 after the last product (not between the
+      // barrier and the first operand reads, nor inside the product run); it
+      // lands during the next step's S/dP phase
+      if (i == NB - 1 && s + 2 < nsteps) issue_next(nxt);
     }
   };
 
